@@ -1,0 +1,204 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention forward hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input (B=4, H=16,
+N=8192, d=128, non-causal, inputs resident in HBM):
+  blockquant_hadamard(Q), (K) with the seeded sign vector, (V) without,
+  attn_fwd_fp8 on the codes, and attn_fwd_bf16 on bf16 N(0,1) inputs.
+Each launch is bracketed by HIP events on the stream it runs on; the printed
+``value`` is the bf16 attention TFLOP/s (4*B*H*N^2*d per launch over its mean
+event time), with the fp8 figure and the pre-pass GB/s beside it.
+
+Prints ONE JSON line (see the repository's design notes for every field).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time of the oracle baseline sample")
+    p.add_argument("--causal", action="store_true", help="time the causal variant instead")
+    p.add_argument("--N", type=int, default=8192)
+    p.add_argument("--B", type=int, default=4)
+    p.add_argument("--H", type=int, default=16)
+    p.add_argument("--d", type=int, default=128)
+    return p.parse_args()
+
+
+def cpu_baseline(w, target_s: float):
+    """Time the fp64 CPU oracle on whole (b, h) heads of the workload until
+    ``target_s`` seconds have passed; report TFLOP/s with the same flop count."""
+    import numpy as np
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    rng = np.random.default_rng(w.seed)
+    heads = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < target_s and heads < w.B * w.H:
+        q, k, v = (workloads.to_bf16_f32(rng.standard_normal((1, w.N, 1, w.d), dtype=np.float32))
+                   for _ in range(3))
+        t1 = time.perf_counter()
+        oracle.naive_attention(q, k, v, w.softmax_scale, w.causal, row_chunk=1024)
+        heads += 1
+        if heads == 1:
+            first = time.perf_counter() - t1
+    el = time.perf_counter() - t0
+    flops = 4.0 * heads * w.N * w.N * w.d / (2 if w.causal else 1)
+    return {
+        "value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"{heads} of {w.B * w.H} (b,h) heads of N={w.N} d={w.d}"
+                  f"{' causal' if w.causal else ''}, fp64 numpy naive attention, {el:.1f} s "
+                  f"(first head {first:.1f} s); input generation included",
+        "host_cpus": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: attention heads are independent and this build "
+              "has no multi-GPU path (see the sharding notes in the design document).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_attention_74_amd as ea
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w16 = workloads.Workload(f"attn_fwd_b{a.B}h{a.H}n{a.N}d{a.d}" + ("_causal" if a.causal else ""),
+                             a.B, a.H, a.N, a.d, a.causal, seed=3)
+    w8 = workloads.Workload(w16.name + "_fp8_outlier30", a.B, a.H, a.N, a.d, a.causal, seed=3,
+                            dist="outlier30")
+
+    def dev_bf16(x):
+        return torch.from_numpy(x).to(torch.bfloat16).to(dev)
+
+    q, k, v = (dev_bf16(x) for x in workloads.gen_qkv(w16))
+    q8in, k8in, v8in = (dev_bf16(x) for x in workloads.gen_qkv(w8))
+    signs = torch.from_numpy(workloads.gen_signs(a.d)).to(dev)
+    B, H, N, d = a.B, a.H, a.N, a.d
+    nsb = (N + 127) // 128
+    o16 = torch.empty_like(q)
+    lse16 = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    o8 = torch.empty_like(q)
+    lse8 = torch.empty_like(lse16)
+    codes = [torch.empty((B, N, H, d), dtype=torch.uint8, device=dev) for _ in range(3)]
+    scales = [torch.empty((B, H, nsb), dtype=torch.float32, device=dev) for _ in range(3)]
+    scale = w16.softmax_scale
+    stream = torch.cuda.current_stream(dev)
+
+    names = ["blockquant_q", "blockquant_k", "blockquant_v", "attn_fwd_fp8", "attn_fwd_bf16"]
+
+    def step(evs=None):
+        calls = [
+            lambda: ea.blockquant_hadamard(q8in, signs, 128, out=codes[0], scale=scales[0]),
+            lambda: ea.blockquant_hadamard(k8in, signs, 128, out=codes[1], scale=scales[1]),
+            lambda: ea.blockquant_hadamard(v8in, None, 128, out=codes[2], scale=scales[2]),
+            lambda: ea.attn_fwd_fp8(codes[0], codes[1], codes[2], *scales, causal=a.causal,
+                                    softmax_scale=scale, out=o8, lse=lse8),
+            lambda: ea.attn_fwd_bf16(q, k, v, causal=a.causal, softmax_scale=scale, out=o16,
+                                     lse=lse16),
+        ]
+        for i, c in enumerate(calls):
+            if evs is not None:
+                evs[i][0].record(stream)
+            c()
+            if evs is not None:
+                evs[i][1].record(stream)
+
+    print(f"[bench] workload {w16.name}: warmup {a.warmup}", file=sys.stderr, flush=True)
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+               for _ in names] for _ in range(a.steps)]
+    print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(a.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: [events[s][i][0].elapsed_time(events[s][i][1]) for s in range(a.steps)]
+           for i, n in enumerate(names)}
+    mean = {n: float(np.mean(v)) for n, v in per.items()}
+    med = {n: float(np.median(v)) for n, v in per.items()}
+
+    flops = w16.flops()
+    t16 = mean["attn_fwd_bf16"] * 1e-3
+    t8 = mean["attn_fwd_fp8"] * 1e-3
+    tf16 = flops / t16 / 1e12
+    tf8 = flops / t8 / 1e12
+    # pre-pass algorithmic bytes per tensor: read bf16, write e4m3, write fp32 scales
+    bq_bytes = B * N * H * d * (2 + 1) + B * H * nsb * 4
+    t_bq = np.mean([mean["blockquant_q"], mean["blockquant_k"], mean["blockquant_v"]]) * 1e-3
+    ok = bool(torch.isfinite(o16).all().item() and torch.isfinite(o8).all().item())
+
+    out = {
+        "metric": "attention fwd TFLOP/s (bf16 & fp8, d=128, N=8k) + % of MFMA peak",
+        "value": round(tf16, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(wall / a.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16; fp8 leg: N(0,1) with 0.1% entries x30)",
+        "config": {"workload": w16.name, "B": B, "H": H, "N": N, "d": d, "causal": a.causal,
+                   "softmax_scale": scale, "global_batch": B, "seq_len": N,
+                   "parallelism": "single GPU (heads and query blocks across CUs)"},
+        "pct_of_peak": round(100 * tf16 / PEAK_BF16_TFLOPS, 2),
+        "fp8": {"value": round(tf8, 2), "unit": "TFLOP/s", "dtype": "fp8 e4m3",
+                "pct_of_peak": round(100 * tf8 / PEAK_FP8_TFLOPS, 2),
+                "workload": w8.name, "ms": round(mean["attn_fwd_fp8"], 4)},
+        "blockquant_hadamard": {"gbps": round(bq_bytes / t_bq / 1e9, 1),
+                                "pct_of_hbm_peak": round(100 * bq_bytes / t_bq / 1e9 / PEAK_HBM_GBS, 2),
+                                "bytes_per_launch": bq_bytes, "us": round(t_bq * 1e6, 2)},
+        "kernel_ms_mean": {n: round(v, 4) for n, v in mean.items()},
+        "kernel_ms_median": {n: round(v, 4) for n, v in med.items()},
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_bf16", "achieved": round(tf16, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf16 / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": flops},
+        "outputs_finite": ok,
+    }
+    if not a.no_cpu_baseline:
+        print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w16, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,155 @@
+"""exact_attention_74_amd: fused exact attention forward (bf16 and FP8) for MI355X.
+
+Thin ctypes binding over ``libexattn.so`` (C ABI declared in include/exattn.h).
+The functions here only check and marshal torch tensors (device pointers,
+shapes, the current HIP stream); every step of the computation runs in the
+library's gfx950 kernels.  There is no CPU or eager fallback: if the library is
+missing or fails to load, every call raises.
+
+Entry points (same names as the C ABI):
+  attn_fwd_bf16(q, k, v, causal=False, softmax_scale=None) -> (o, lse)
+  blockquant_hadamard(x, signs=None, block_rows=128) -> (x8, scale)
+  attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal=False, softmax_scale=None) -> (o, lse)
+Tensors are BSHD (batch, seqlen, heads, head_dim), contiguous, on a HIP device.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libexattn.so")
+
+_c_void_p = ctypes.c_void_p
+_c_int = ctypes.c_int
+_c_float = ctypes.c_float
+
+# (name, argtypes) for every symbol of include/exattn.h
+SIGNATURES = {
+    "attn_fwd_bf16": [_c_void_p] * 5 + [_c_int] * 5 + [_c_float, _c_void_p],
+    "attn_fwd_fp8": [_c_void_p] * 8 + [_c_int] * 5 + [_c_float, _c_void_p],
+    "blockquant_hadamard": [_c_void_p] * 4 + [_c_int] * 5 + [_c_void_p],
+    "exattn_strerror": [_c_int],
+    "exattn_abi_version": [],
+}
+RESTYPES = {"exattn_strerror": ctypes.c_char_p}
+
+ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_VALUE, ERR_HIP = -1, -2, -3, -4, -5
+
+_lib = None
+
+
+class ExattnError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        super().__init__(f"{fn} failed with code {code}: {strerror(code)}")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libexattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with "
+                               "`python -m exact_attention_74_amd.build` (no fallback exists)")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, args in SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.argtypes = args
+            fn.restype = RESTYPES.get(name, _c_int)
+        _lib = h
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().exattn_strerror(int(code)).decode()
+
+
+def _stream_ptr(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _check_bshd(name: str, t: torch.Tensor, dtype) -> tuple[int, int, int, int]:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device (got {t.device})")
+    if t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} must have dtype {dtype} (got {t.dtype})")
+    if t.dim() != 4 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous 4-D BSHD tensor")
+    return tuple(t.shape)
+
+
+def _call(fn: str, *args) -> None:
+    rc = getattr(lib(), fn)(*args)
+    if rc != 0:
+        raise ExattnError(fn, rc)
+
+
+def attn_fwd_bf16(q, k, v, causal: bool = False, softmax_scale: float | None = None,
+                  out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """O = softmax(scale Q K^T [causal]) V in bf16; returns (O bf16 BSHD, LSE fp32 [B,H,N])."""
+    shape = _check_bshd("q", q, torch.bfloat16)
+    if _check_bshd("k", k, torch.bfloat16) != shape or _check_bshd("v", v, torch.bfloat16) != shape:
+        raise ValueError("q, k, v must have the same shape")
+    B, N, H, d = shape
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _call("attn_fwd_bf16", q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+          B, H, N, d, int(bool(causal)), scale, _stream_ptr(q))
+    return out, lse
+
+
+def blockquant_hadamard(x, signs: torch.Tensor | None = None, block_rows: int = 128,
+                        out: torch.Tensor | None = None, scale: torch.Tensor | None = None):
+    """Rotate (if ``signs``) and block-quantise a bf16 BSHD tensor to e4m3.
+
+    Returns (codes uint8 BSHD, scale fp32 [B, H, ceil(N/128)]).
+    """
+    B, N, H, d = _check_bshd("x", x, torch.bfloat16)
+    if signs is not None:
+        if signs.device != x.device or signs.dtype != torch.float32 or signs.numel() != d:
+            raise ValueError("signs must be d float32 values on the same device")
+        signs = signs.contiguous()
+    if out is None:
+        out = torch.empty((B, N, H, d), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty((B, H, (N + 127) // 128), dtype=torch.float32, device=x.device)
+    _call("blockquant_hadamard", x.data_ptr(), out.data_ptr(), scale.data_ptr(),
+          signs.data_ptr() if signs is not None else None, B, H, N, d, int(block_rows),
+          _stream_ptr(x))
+    return out, scale
+
+
+def attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False,
+                 softmax_scale: float | None = None, out: torch.Tensor | None = None,
+                 lse: torch.Tensor | None = None):
+    """FP8 attention on e4m3 codes (uint8 or float8_e4m3fn) with block scales."""
+    codes = (torch.uint8, torch.float8_e4m3fn)
+    shape = _check_bshd("q8", q8, codes)
+    if _check_bshd("k8", k8, codes) != shape or _check_bshd("v8", v8, codes) != shape:
+        raise ValueError("q8, k8, v8 must have the same shape")
+    B, N, H, d = shape
+    nsb = (N + 127) // 128
+    for name, s in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
+        if s.dtype != torch.float32 or tuple(s.shape) != (B, H, nsb) or not s.is_contiguous():
+            raise ValueError(f"{name} must be contiguous float32 [B, H, ceil(N/128)]")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((B, N, H, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    _call("attn_fwd_fp8", q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), q_scale.data_ptr(),
+          k_scale.data_ptr(), v_scale.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+          int(bool(causal)), scale, _stream_ptr(q8))
+    return out, lse
+
+
+__all__ = ["attn_fwd_bf16", "attn_fwd_fp8", "blockquant_hadamard", "lib", "strerror",
+           "ExattnError", "LIB_PATH", "SIGNATURES"]

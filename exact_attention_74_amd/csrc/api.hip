@@ -1,0 +1,109 @@
+// C ABI of libexattn.so: argument validation, then dispatch to the gfx950
+// launchers.  Every check runs before the first HIP call, so a rejected call
+// launches nothing and touches no output.
+#include <math.h>
+#include <stdint.h>
+
+#include "exattn.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kMaxN = int64_t(1) << 24;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Byte ranges [a, a+na) and [b, b+nb) overlap.
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
+}
+
+int check_shape(int B, int H, int N, int d) {
+  if (B < 0 || H < 0 || N < 0) return EXATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return EXATTN_ERR_SHAPE;
+  if ((int64_t)N >= kMaxN) return EXATTN_ERR_SHAPE;
+  const int64_t blocks = (int64_t)B * H * (((int64_t)N + 127) / 128);
+  if (blocks >= (int64_t(1) << 31)) return EXATTN_ERR_SHAPE;
+  return EXATTN_OK;
+}
+
+bool good_scale(float s) { return isfinite(s) && s > 0.f; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? EXATTN_OK : EXATTN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int exattn_abi_version(void) { return 1; }
+
+const char* exattn_strerror(int code) {
+  switch (code) {
+    case EXATTN_OK: return "success";
+    case EXATTN_ERR_NULL: return "a required pointer is NULL";
+    case EXATTN_ERR_SHAPE: return "unsupported shape (negative size, d not in {64,128}, or too large)";
+    case EXATTN_ERR_ALIGN: return "pointer not aligned (tensors 16 bytes, scales/LSE 4 bytes)";
+    case EXATTN_ERR_VALUE: return "invalid value (softmax_scale, causal, block_rows, or aliasing output)";
+    case EXATTN_ERR_HIP: return "HIP error (no device or kernel launch failed)";
+    default: return "unknown error code";
+  }
+}
+
+int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                  int N, int d, int causal, float softmax_scale, void* stream) {
+  int rc = check_shape(B, H, N, d);
+  if (rc) return rc;
+  if ((causal != 0 && causal != 1) || !good_scale(softmax_scale)) return EXATTN_ERR_VALUE;
+  const int64_t bytes = (int64_t)B * N * H * d * 2;
+  if (bytes == 0) return EXATTN_OK;
+  if (!q || !k || !v || !o) return EXATTN_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      (lse && !aligned(lse, 4)))
+    return EXATTN_ERR_ALIGN;
+  if (overlap(o, bytes, q, bytes) || overlap(o, bytes, k, bytes) || overlap(o, bytes, v, bytes))
+    return EXATTN_ERR_VALUE;
+  if (lse && overlap(lse, (int64_t)B * H * N * 4, o, bytes)) return EXATTN_ERR_VALUE;
+  return hip_status(exattn::launch_attn_fwd_bf16(q, k, v, o, lse, B, H, N, d, causal != 0,
+                                                 softmax_scale, (hipStream_t)stream));
+}
+
+int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_scale,
+                 const float* k_scale, const float* v_scale, void* o, float* lse, int B, int H,
+                 int N, int d, int causal, float softmax_scale, void* stream) {
+  int rc = check_shape(B, H, N, d);
+  if (rc) return rc;
+  if ((causal != 0 && causal != 1) || !good_scale(softmax_scale)) return EXATTN_ERR_VALUE;
+  const int64_t in_bytes = (int64_t)B * N * H * d;
+  if (in_bytes == 0) return EXATTN_OK;
+  if (!q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale || !o) return EXATTN_ERR_NULL;
+  if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8, 16) || !aligned(o, 16) ||
+      !aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4) ||
+      (lse && !aligned(lse, 4)))
+    return EXATTN_ERR_ALIGN;
+  const int64_t out_bytes = 2 * in_bytes;
+  if (overlap(o, out_bytes, q8, in_bytes) || overlap(o, out_bytes, k8, in_bytes) ||
+      overlap(o, out_bytes, v8, in_bytes))
+    return EXATTN_ERR_VALUE;
+  if (lse && overlap(lse, (int64_t)B * H * N * 4, o, out_bytes)) return EXATTN_ERR_VALUE;
+  return hip_status(exattn::launch_attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B,
+                                                H, N, d, causal != 0, softmax_scale,
+                                                (hipStream_t)stream));
+}
+
+int blockquant_hadamard(const void* x, void* x8, float* scale, const float* signs, int B, int H,
+                        int N, int d, int block_rows, void* stream) {
+  int rc = check_shape(B, H, N, d);
+  if (rc) return rc;
+  if (block_rows != 0 && block_rows != 128) return EXATTN_ERR_VALUE;
+  const int64_t n = (int64_t)B * N * H * d;
+  if (n == 0) return EXATTN_OK;
+  if (!x || !x8 || !scale) return EXATTN_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(x8, 16) || !aligned(scale, 4) || (signs && !aligned(signs, 4)))
+    return EXATTN_ERR_ALIGN;
+  if (overlap(x8, n, x, 2 * n)) return EXATTN_ERR_VALUE;
+  return hip_status(
+      exattn::launch_blockquant(x, x8, scale, signs, B, H, N, d, block_rows, (hipStream_t)stream));
+}
+
+}  // extern "C"

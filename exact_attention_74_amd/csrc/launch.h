@@ -1,0 +1,21 @@
+// Host-side launchers of the gfx950 kernels.  Arguments are validated by the
+// C ABI layer before any of these is called; each launcher only enqueues work
+// on `stream` and returns the HIP status of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace exattn {
+
+hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int H, int N, int d, bool causal, float softmax_scale,
+                                hipStream_t stream);
+
+hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* sq,
+                               const float* sk, const float* sv, void* o, float* lse, int B, int H,
+                               int N, int d, bool causal, float softmax_scale, hipStream_t stream);
+
+hipError_t launch_blockquant(const void* x, void* x8, float* scale, const float* signs, int B, int H,
+                             int N, int d, int block_rows, hipStream_t stream);
+
+}  // namespace exattn

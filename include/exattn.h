@@ -1,0 +1,122 @@
+/*
+ * exattn -- fused exact attention forward for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libexattn.so.  Plain pointers and sizes only.
+ *
+ * The operation is exact softmax attention,
+ *     O = softmax(scale * Q K^T [+ causal mask]) V,
+ * computed tile by tile with the online-softmax recurrence (running row max m
+ * and row sum l, one final normalisation) so that the N x N score matrix never
+ * reaches device memory ("深度解读报告：FlashAttention-3（2024）", zako-mio
+ * knowledge base, section 3 and section 3.1-3.2; "Efficient Attention &
+ * FlashAttention", talentme M4-054, FA2's query-block parallelism and single
+ * final normalisation).  The FP8 entry points implement the report's section
+ * 3.3 low-precision scheme: per-block scales on Q, K and V and incoherent
+ * processing (Q and K multiplied by a random +-1 diagonal times a Hadamard
+ * matrix, which leaves Q K^T unchanged).
+ *
+ * Conventions shared by every entry point
+ *   Layout      Q, K, V and O are BSHD: (batch B, seqlen N, heads H, head dim d),
+ *               contiguous, the layout of the FlashAttention-3 Python
+ *               interface (0539edu blog on FlashAttention V3, section 4.2).
+ *               Element (b, n, h, c) is at ((b*N + n)*H + h)*d + c.
+ *   Sizes       B, H, N >= 0 (any of them 0: nothing to do, returns 0 once
+ *               the sizes and values are valid; pointers may then be NULL);
+ *               d in {64, 128} (other head dims are zero-padded by the caller
+ *               to 64 or 128, keeping softmax_scale = 1/sqrt(d_original); the
+ *               same blog, section 3.1); B*H*ceil(N/128) < 2^31; N < 2^24.
+ *   Memory      every pointer is device memory owned by the caller; the
+ *               library allocates and frees nothing and keeps no state
+ *               between calls.  Tensor pointers must be 16-byte aligned
+ *               (64-byte alignment is recommended), scale/LSE pointers 4-byte.
+ *   Streams     every call is asynchronous on `stream` (a hipStream_t; NULL is
+ *               the default stream).  Device faults surface at the caller's
+ *               next synchronisation.
+ *   Errors      0 on success, a negative EXATTN_ERR_* code otherwise.  All
+ *               arguments are validated before any HIP call, in the order
+ *               sizes, values, empty problem, NULL, alignment, aliasing; on a validation
+ *               error nothing is launched and no output is touched.  No C++
+ *               exception crosses the ABI.  Thread-safe.
+ *   Causal      key j is visible to query i iff j <= i.
+ *   Outputs     O is bfloat16 (round to nearest even from fp32);
+ *               LSE[b, h, i] = ln sum_j exp(scale * q_i . k_j) over visible
+ *               keys, fp32, laid out [B, H, N] (the softmax statistic kept for
+ *               a backward pass, 0539edu blog section 5.4).  lse may be NULL.
+ */
+#ifndef EXATTN_H
+#define EXATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EXATTN_OK 0
+#define EXATTN_ERR_NULL (-1)  /* a required pointer is NULL                        */
+#define EXATTN_ERR_SHAPE (-2) /* negative size, unsupported d, or too large       */
+#define EXATTN_ERR_ALIGN (-3) /* a pointer is not aligned as required             */
+#define EXATTN_ERR_VALUE (-4) /* softmax_scale not finite and > 0, bad block_rows */
+#define EXATTN_ERR_HIP (-5)   /* no HIP device, or a launch failed                */
+
+/*
+ * bf16 attention forward.
+ *   q, k, v      bfloat16 BSHD inputs.
+ *   o            bfloat16 BSHD output (must not alias q, k or v).
+ *   lse          fp32 [B, H, N] output, or NULL.
+ *   causal       0 or 1.
+ *   softmax_scale  multiplies Q K^T; finite and > 0 (usually 1/sqrt(d)).
+ * The score matrix is never materialised: each workgroup owns a block of
+ * query rows of one (b, h) and streams K/V blocks through LDS.
+ */
+int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int N, int d, int causal, float softmax_scale, void* stream);
+
+/*
+ * FP8 (OCP e4m3) attention forward, FlashAttention-3 report section 3.3.
+ *   q8, k8, v8   e4m3 codes, BSHD (one byte per element), as written by
+ *                blockquant_hadamard (Q and K rotated with the same signs).
+ *   q_scale, k_scale, v_scale   fp32 [B, H, ceil(N/128)]: the dequantised value
+ *                of element (b, n, h, c) is code * scale[b, h, n / 128].
+ *   o, lse, causal, softmax_scale   as in attn_fwd_bf16.
+ * Each score tile is scaled by q_scale * k_scale * softmax_scale; the softmax
+ * probabilities are rounded to e4m3 for the P.V product; V scales are folded
+ * into the output rescaling.  Accumulation is fp32.
+ */
+int attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
+                 const float* q_scale, const float* k_scale, const float* v_scale,
+                 void* o, float* lse,
+                 int B, int H, int N, int d, int causal, float softmax_scale, void* stream);
+
+/*
+ * FP8 pre-pass: optional incoherent rotation, then block quantisation to e4m3
+ * (FlashAttention-3 report, sections 2.2 and 3.3).
+ *   x        bfloat16 BSHD input.
+ *   x8       e4m3 BSHD output (one byte per element).
+ *   scale    fp32 [B, H, ceil(N/128)] output.
+ *   signs    d floats, each +1 or -1, device memory; NULL = no rotation.
+ *   block_rows  128: one scale per 128-row x d block of each (b, h);
+ *               0: one scale for the whole tensor, written to every slot
+ *               (the per-tensor baseline).
+ * With signs, y = x diag(signs) H_d (Sylvester Hadamard, unnormalised fast
+ * Walsh-Hadamard transform, butterfly strides 1, 2, 4, ... in fp32), and the
+ * stored scale carries the 1/sqrt(d) of the orthonormal rotation.  Without
+ * signs, y = x.  Per block: amax = max |y|; r = 448 / amax (fp32);
+ * code = e4m3_rne(y * r); scale = amax / 448 (/ sqrt(d) when rotated).  A block
+ * with amax 0 gets scale 1 and all-zero codes.  Dequantised: code * scale
+ * approximates x M with M = diag(signs) H_d / sqrt(d), M M^T = I.
+ * block_rows = 0 launches three kernels (block amax, global max, quantise);
+ * otherwise one.
+ */
+int blockquant_hadamard(const void* x, void* x8, float* scale, const float* signs,
+                        int B, int H, int N, int d, int block_rows, void* stream);
+
+/* Static, never-NULL description of a return code. */
+const char* exattn_strerror(int code);
+
+/* Library ABI version (increments on any signature or semantic change). */
+int exattn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXATTN_H */

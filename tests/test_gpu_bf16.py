@@ -1,0 +1,165 @@
+"""bf16 attention forward on the GPU vs the fp64 CPU oracle.
+
+Gate (both masks): max-abs error <= 1e-2 and RMSE <= 2e-3 on N(0,1) inputs, the
+stated bf16 tolerance.  Tighter internal gates (max-abs <= 4e-3, RMSE <= 5e-4,
+LSE <= 2e-4) catch kernel bugs that the stated tolerance would let through:
+bf16 rounding of P and of O alone stays well below them.  The oracle sees the
+same bf16-rounded inputs upcast to fp64, so the gate measures the kernel, not
+the input rounding.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_helpers import (DEV, bf16_inputs, err_stats, lse_rows, rows_of, say, to_dev_bf16, to_np)
+
+import exact_attention_74_amd as ea
+
+pytestmark = pytest.mark.gpu
+
+GATE_MAX, GATE_RMSE = 1e-2, 2e-3
+INT_MAX, INT_RMSE, INT_LSE = 4e-3, 5e-4, 2e-4
+
+
+def _check(o, lse, o_ref, lse_ref, tag):
+    mx, rmse = err_stats(o, o_ref)
+    lerr = float(np.abs(lse - lse_ref).max())
+    print(f"{tag}: max_abs={mx:.3e} rmse={rmse:.3e} lse_max={lerr:.3e}", flush=True)
+    assert mx <= GATE_MAX and rmse <= GATE_RMSE, (mx, rmse)
+    assert mx <= INT_MAX and rmse <= INT_RMSE and lerr <= INT_LSE, (mx, rmse, lerr)
+
+
+def _run(dev_qkv, causal, scale):
+    o, lse = ea.attn_fwd_bf16(*dev_qkv, causal=causal, softmax_scale=scale)
+    torch.cuda.synchronize()
+    return to_np(o), lse.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_tiny_full_parity(causal):
+    w = workloads.TINY_CAUSAL if causal else workloads.TINY
+    say(w.name)
+    host, dev = bf16_inputs(w)
+    o, lse = _run(dev, causal, w.softmax_scale)
+    o_ref, lse_ref = oracle.naive_attention(*host, w.softmax_scale, causal)
+    _check(o, lse, o_ref, lse_ref, w.name)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 37, 64, 129, 1000])
+def test_ragged_full_parity(causal, d, N):
+    """Several query/key tiles with a ragged tail (N not a multiple of 64/128)."""
+    w = workloads.Workload(f"ragged_n{N}_d{d}", 2, 3, N, d, causal, seed=11 + N)
+    say(w.name + ("_causal" if causal else ""))
+    host, dev = bf16_inputs(w)
+    o, lse = _run(dev, causal, w.softmax_scale)
+    o_ref, lse_ref = oracle.naive_attention(*host, w.softmax_scale, causal)
+    _check(o, lse, o_ref, lse_ref, w.name)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_d96_zero_padded(causal):
+    """d=96 zero-padded to 128 with scale 1/sqrt(96) equals d=96 attention."""
+    w = workloads.Workload("pad96", 2, 4, 700, 128, causal, seed=21, d_logical=96)
+    say(w.name)
+    host, dev = bf16_inputs(w)
+    o, lse = _run(dev, causal, w.softmax_scale)
+    o_ref, lse_ref = oracle.naive_attention(*(x[..., :96] for x in host), 1 / math.sqrt(96), causal)
+    _check(o[..., :96], lse, o_ref, lse_ref, w.name)
+    assert np.all(o[..., 96:] == 0.0)
+
+
+@pytest.mark.parametrize("w", [workloads.MID, workloads.MID_CAUSAL, workloads.LONG],
+                         ids=lambda w: w.name)
+def test_full_size_sampled_rows(w):
+    say(w.name)
+    host, dev = bf16_inputs(w)
+    o, lse = _run(dev, w.causal, w.softmax_scale)
+    rows = workloads.sample_rows(w.B, w.H, w.N, 1024, seed=w.seed + 100)
+    o_ref, l_ref = oracle.naive_attention_rows(*host, w.softmax_scale, w.causal, rows)
+    _check(rows_of(o, rows), lse_rows(lse, rows), o_ref, l_ref, w.name)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("w", [x for x in workloads.sweep(False) + workloads.sweep(True)
+                               if x.N in (512, 8192, 16384)], ids=lambda w: w.name)
+def test_sweep_sampled_rows(w):
+    say(w.name)
+    host, dev = bf16_inputs(w)
+    o, lse = _run(dev, w.causal, w.softmax_scale)
+    rows = workloads.sample_rows(w.B, w.H, w.N, 512, seed=w.N)
+    dl = w.d_logical or w.d
+    o_ref, l_ref = oracle.naive_attention_rows(*(x[..., :dl] for x in host), w.softmax_scale,
+                                               w.causal, rows)
+    _check(rows_of(o, rows)[:, :dl], lse_rows(lse, rows), o_ref, l_ref, w.name)
+
+
+def test_causal_row0_equals_v0_bitwise():
+    w = workloads.Workload("row0", 2, 4, 300, 128, True, seed=31)
+    say(w.name)
+    host, dev = bf16_inputs(w)
+    o, _ = ea.attn_fwd_bf16(*dev, causal=True)
+    assert torch.equal(o[:, 0], dev[2][:, 0])
+
+
+def test_identical_value_rows():
+    w = workloads.Workload("vrows", 1, 2, 513, 64, False, seed=32)
+    say(w.name)
+    host, dev = bf16_inputs(w)
+    row = workloads.to_bf16_f32(workloads.gen_random((64,), 33))
+    v = np.broadcast_to(row, host[2].shape).copy()
+    o, _ = ea.attn_fwd_bf16(dev[0], dev[1], to_dev_bf16(v), causal=False)
+    torch.cuda.synchronize()
+    assert np.abs(to_np(o) - row).max() <= 4e-3 * max(1.0, np.abs(row).max())
+
+
+def test_causal_prefix_independence_bitwise():
+    w = workloads.Workload("prefix", 1, 2, 640, 128, True, seed=34)
+    say(w.name)
+    host, dev = bf16_inputs(w)
+    o1, l1 = ea.attn_fwd_bf16(*dev, causal=True)
+    k2, v2 = host[1].copy(), host[2].copy()
+    k2[:, 300:] += 3.0
+    v2[:, 300:] *= -2.0
+    o2, l2 = ea.attn_fwd_bf16(dev[0], to_dev_bf16(k2), to_dev_bf16(v2), causal=True)
+    assert torch.equal(o1[:, :300], o2[:, :300])
+    assert torch.equal(l1[:, :, :300], l2[:, :, :300])
+    assert not torch.equal(o1[:, 300:], o2[:, 300:])
+
+
+def test_deterministic_bitwise():
+    w = workloads.Workload("determinism", 2, 8, 2048, 128, False, seed=35)
+    say(w.name)
+    _, dev = bf16_inputs(w)
+    o1, l1 = ea.attn_fwd_bf16(*dev)
+    o2, l2 = ea.attn_fwd_bf16(*dev)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_lse_none_and_stream():
+    """lse=NULL is accepted at the ABI, and work goes to the caller's stream."""
+    w = workloads.Workload("stream", 1, 2, 256, 64, False, seed=36)
+    say(w.name)
+    host, dev = bf16_inputs(w)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o = torch.empty_like(dev[0])
+        rc = ea.lib().attn_fwd_bf16(dev[0].data_ptr(), dev[1].data_ptr(), dev[2].data_ptr(),
+                                    o.data_ptr(), None, 1, 2, 256, 64, 0, 0.125, s.cuda_stream)
+    s.synchronize()
+    assert rc == 0
+    o_ref, _ = oracle.naive_attention(*host, 0.125, False)
+    mx, rmse = err_stats(to_np(o), o_ref)
+    assert mx <= INT_MAX and rmse <= INT_RMSE
+
+
+def test_empty_problem_is_noop():
+    say("empty")
+    z = torch.empty((0, 128, 2, 64), dtype=torch.bfloat16, device=DEV)
+    o, lse = ea.attn_fwd_bf16(z, z, z)
+    assert o.shape == z.shape and lse.numel() == 0

@@ -1,0 +1,176 @@
+"""FP8 path on the GPU vs the CPU oracle.
+
+blockquant_hadamard: e4m3 codes bit-exact and scales equal to the oracle's
+emulation of the pre-pass (both take the quantise decision in fp32, with the
+same butterfly order).
+
+attn_fwd_fp8 (fed the oracle's own codes and scales):
+  * tight gate vs the oracle's FP8 emulation: RMSE(GPU - emulation) <= 0.1 x
+    RMSE(emulation - exact);
+  * vs exact fp64 attention on the unrotated bf16 inputs: RMSE <= 3e-2 on the
+    outlier distribution of the FlashAttention-3 report (section 4.3), and
+    below the per-tensor-scaled run without rotation on both outlier
+    distributions.  On the x30-outlier workload the measured RMSE is reported
+    next to the emulation floor of the scheme (about 9e-2, above 3e-2).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_helpers import DEV, err_stats, say, to_np
+
+import exact_attention_74_amd as ea
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_host(w):
+    return [workloads.to_bf16_f32(x) for x in workloads.gen_qkv(w)]
+
+
+def _dev_bf16(x):
+    return torch.from_numpy(x).to(torch.bfloat16).to(DEV)
+
+
+def _gpu_quant(x_host, signs, block_rows):
+    s = None if signs is None else torch.from_numpy(signs).to(DEV)
+    c, sc = ea.blockquant_hadamard(_dev_bf16(x_host), s, block_rows)
+    torch.cuda.synchronize()
+    return c.cpu().numpy(), sc.cpu().numpy()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 130, 300, 1024])
+@pytest.mark.parametrize("rotate", [True, False])
+@pytest.mark.parametrize("block_rows", [128, 0])
+def test_blockquant_bit_exact(d, N, rotate, block_rows):
+    say(f"blockquant d{d} N{N} rot{rotate} br{block_rows}")
+    w = workloads.Workload("bq", 2, 3, N, d, False, seed=40 + N, dist="outlier30")
+    x = _bf16_host(w)[0]
+    signs = workloads.gen_signs(d) if rotate else None
+    c_gpu, s_gpu = _gpu_quant(x, signs, block_rows)
+    c_ref, s_ref = oracle.blockquant_hadamard(x, signs, block_rows)
+    assert np.array_equal(s_gpu, s_ref), np.abs(s_gpu - s_ref).max()
+    assert np.array_equal(c_gpu, c_ref), f"{np.count_nonzero(c_gpu != c_ref)} codes differ"
+
+
+def test_blockquant_full_size_heads():
+    """The fp8 workload's full tensor on the GPU; a few (b, h) heads checked."""
+    w = workloads.FP8
+    say(w.name + " blockquant")
+    x = _bf16_host(w)[0]
+    signs = workloads.gen_signs(w.d)
+    c_gpu, s_gpu = _gpu_quant(x, signs, 128)
+    for b, h in ((0, 0), (1, 7), (3, 15)):
+        c_ref, s_ref = oracle.blockquant_hadamard(x[b:b + 1, :, h:h + 1], signs, 128)
+        assert np.array_equal(s_gpu[b:b + 1, h:h + 1], s_ref)
+        assert np.array_equal(c_gpu[b:b + 1, :, h:h + 1], c_ref)
+
+
+def test_blockquant_zero_block_and_signs_identity():
+    say("blockquant zero block")
+    x = workloads.to_bf16_f32(workloads.gen_random((1, 256, 2, 64), 41))
+    x[:, :128] = 0.0
+    c, s = _gpu_quant(x, workloads.gen_signs(64), 128)
+    assert np.all(s[:, :, 0] == 1.0) and not c[:, :128].any()
+
+
+def _quant_all(q, k, v, signs, block_rows):
+    """The oracle's codes and scales for Q, K (rotated if signs) and V."""
+    q8, sq = oracle.blockquant_hadamard(q, signs, block_rows)
+    k8, sk = oracle.blockquant_hadamard(k, signs, block_rows)
+    v8, sv = oracle.blockquant_hadamard(v, None, block_rows)
+    return q8, k8, v8, sq, sk, sv
+
+
+def _gpu_fp8(q8, k8, v8, sq, sk, sv, scale, causal):
+    t = [torch.from_numpy(np.ascontiguousarray(a)).to(DEV) for a in (q8, k8, v8, sq, sk, sv)]
+    o, lse = ea.attn_fwd_fp8(*t, causal=causal, softmax_scale=scale)
+    torch.cuda.synchronize()
+    return to_np(o), lse.cpu().numpy().astype(np.float64)
+
+
+def _rmse(a, b):
+    return float(np.sqrt(np.mean((np.asarray(a, np.float64) - b) ** 2)))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [100, 256, 1000])
+def test_fp8_attention_vs_emulation_full(causal, d, N):
+    w = workloads.Workload(f"fp8_n{N}_d{d}", 2, 3, N, d, causal, seed=50 + N, dist="outlier_sd10")
+    say(w.name + ("_causal" if causal else ""))
+    q, k, v = _bf16_host(w)
+    signs = workloads.gen_signs(d)
+    qs = _quant_all(q, k, v, signs, 128)
+    o, lse = _gpu_fp8(*qs, w.softmax_scale, causal)
+    o_em, l_em = oracle.fp8_attention_emulation(*qs, w.softmax_scale, causal)
+    o_ex, l_ex = oracle.naive_attention(q, k, v, w.softmax_scale, causal)
+    e_kernel = _rmse(o, o_em)
+    e_scheme = _rmse(o_em, o_ex)
+    lerr = float(np.abs(lse - l_em).max())
+    print(f"{w.name}: rmse(gpu-emul)={e_kernel:.3e} rmse(emul-exact)={e_scheme:.3e} "
+          f"rmse(gpu-exact)={_rmse(o, o_ex):.3e} lse(gpu-emul)={lerr:.3e}", flush=True)
+    assert e_kernel <= 0.1 * e_scheme
+    assert lerr <= 1e-3
+    assert np.isfinite(o).all()
+
+
+@pytest.mark.parametrize("w", [workloads.FP8_PAGE, workloads.FP8], ids=lambda w: w.name)
+def test_fp8_full_size_rows_and_baseline(w):
+    """Full fp8 workload on the GPU (pre-pass and attention); 128 sampled rows
+    in each of four (b, h) heads checked.  Blocks never straddle heads, so the
+    oracle quantises just those heads."""
+    say(w.name)
+    q, k, v = _bf16_host(w)
+    signs = workloads.gen_signs(w.d)
+    ts = torch.from_numpy(signs).to(DEV)
+    tq, tk, tv = (_dev_bf16(x) for x in (q, k, v))
+
+    def gpu_path(sg, br):
+        q8, sq = ea.blockquant_hadamard(tq, sg, br)
+        k8, sk = ea.blockquant_hadamard(tk, sg, br)
+        v8, sv = ea.blockquant_hadamard(tv, None, br)
+        o, _ = ea.attn_fwd_fp8(q8, k8, v8, sq, sk, sv, softmax_scale=w.softmax_scale)
+        torch.cuda.synchronize()
+        return to_np(o)
+
+    o_fa3 = gpu_path(ts, 128)
+    o_base = gpu_path(None, 0)
+    got_fa3, got_base, ref_ex, ref_em = [], [], [], []
+    for b, h in ((0, 0), (1, 5), (2, 10), (3, 15)):
+        sl = [x[b:b + 1, :, h:h + 1] for x in (q, k, v)]
+        rows = workloads.sample_rows(1, 1, w.N, 128, seed=77 + h)
+        o_ex, _ = oracle.naive_attention_rows(*sl, w.softmax_scale, False, rows)
+        o_em, _ = oracle.fp8_attention_emulation(*_quant_all(*sl, signs, 128), w.softmax_scale,
+                                                 False, rows=rows)
+        i = rows[:, 2]
+        got_fa3.append(o_fa3[b, i, h])
+        got_base.append(o_base[b, i, h])
+        ref_ex.append(o_ex)
+        ref_em.append(o_em)
+    o_fa3, o_base, o_ex, o_em = (np.concatenate(a) for a in (got_fa3, got_base, ref_ex, ref_em))
+    e_fa3, e_base, e_em = _rmse(o_fa3, o_ex), _rmse(o_base, o_ex), _rmse(o_em, o_ex)
+    e_kernel = _rmse(o_fa3, o_em)
+    rel = e_fa3 / float(np.sqrt(np.mean(o_ex ** 2)))
+    print(f"{w.name}: rmse fa3-fp8={e_fa3:.3e} (rel {rel:.3e}) per-tensor/no-rotation={e_base:.3e} "
+          f"emulation floor={e_em:.3e} gpu-vs-emulation={e_kernel:.3e} "
+          f"ratio={e_base / e_fa3:.2f}", flush=True)
+    assert e_kernel <= 0.1 * e_em
+    assert e_fa3 < e_base
+    if w.dist == "outlier_sd10":
+        assert e_fa3 <= 3e-2
+
+
+def test_fp8_lse_vs_exact_normal_inputs():
+    w = workloads.Workload("fp8_normal", 1, 4, 2048, 128, False, seed=60)
+    say(w.name)
+    q, k, v = _bf16_host(w)
+    qs = _quant_all(q, k, v, workloads.gen_signs(128), 128)
+    o, lse = _gpu_fp8(*qs, w.softmax_scale, False)
+    o_ex, l_ex = oracle.naive_attention(q, k, v, w.softmax_scale, False)
+    mx, rmse = err_stats(o, o_ex)
+    print(f"fp8 normal: max={mx:.3e} rmse={rmse:.3e} lse={np.abs(lse - l_ex).max():.3e}")
+    assert rmse <= 3e-3 and np.abs(lse - l_ex).max() <= 5e-2
