@@ -18,7 +18,8 @@ notes of the repository):
     saturating at +-448.
   * Block scale: amax of the block / 448.  The 1/sqrt(d) of M is folded into
     the stored scale, so the codes are taken from the unnormalised transform.
-    A block whose amax is 0 stores scale 1 (all its codes are 0).
+    A block whose amax is 0 stores scale 1; its codes are +-0, the sign of
+    each zero following IEEE-754 arithmetic through the transform.
   * The quantise decision is taken in fp32, the kernel's precision: the
     transform is the textbook butterfly in fp32 with strides 1, 2, 4, ...,
     r = fp32(448 / amax) and code = e4m3(fp32(y * r)).
@@ -62,8 +63,9 @@ _MAGS = _TABLE[:127].copy()  # codes 0x00..0x7E, increasing magnitudes 0 .. 448
 def e4m3_encode(x) -> np.ndarray:
     """Round to the nearest e4m3 code, ties to even, saturating at +-448.
 
-    Works on the exact value of each float32/float64 input (all midpoints of
-    e4m3 are exact in float64).  Returns uint8 codes.  NaN input is rejected.
+    Negative inputs that round to zero give -0 (0x80).  Works on the exact
+    value of each float32/float64 input (all midpoints of e4m3 are exact in
+    float64).  Returns uint8 codes.  NaN input is rejected.
     """
     a = np.asarray(x, dtype=np.float64)
     if np.isnan(a).any():
@@ -76,8 +78,9 @@ def e4m3_encode(x) -> np.ndarray:
     dhi = _MAGS[hi] - mag
     pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
     code = np.where(mag == 0.0, 0, np.where(pick_hi, hi, lo)).astype(np.uint8)
-    neg = np.signbit(a) & (code != 0)
-    return np.where(neg, code | 0x80, code).astype(np.uint8)
+    # the sign bit follows the operand, also when the magnitude rounds to zero
+    # (IEEE-754 rounding keeps the sign; e4m3 has both +0 and -0)
+    return np.where(np.signbit(a), code | 0x80, code).astype(np.uint8)
 
 
 def e4m3_decode(codes) -> np.ndarray:
@@ -158,8 +161,8 @@ def blockquant_hadamard(x, signs=None, block_rows: int = QBLOCK):
 
     def quant(blk):
         amax = np.float32(np.max(np.abs(blk))) if blk.size else np.float32(0)
-        if amax == 0:
-            return np.zeros(blk.shape, np.uint8), np.float32(1.0)
+        if amax == 0:  # all (signed) zeros: coded with r = 1, scale 1
+            return e4m3_encode(blk), np.float32(1.0)
         r = np.float32(E4M3_MAX) / amax
         return e4m3_encode((blk * r).astype(np.float32)), np.float32(amax * kconst)
 
