@@ -74,7 +74,9 @@ def test_blockquant_zero_block_and_signs_identity():
     x = workloads.to_bf16_f32(workloads.gen_random((1, 256, 2, 64), 41))
     x[:, :128] = 0.0
     c, s = _gpu_quant(x, workloads.gen_signs(64), 128)
-    assert np.all(s[:, :, 0] == 1.0) and not c[:, :128].any()
+    assert np.all(s[:, :, 0] == 1.0) and not (c[:, :128] & 0x7F).any()
+    c_ref, s_ref = oracle.blockquant_hadamard(x, workloads.gen_signs(64), 128)
+    assert np.array_equal(c, c_ref) and np.array_equal(s, s_ref)
 
 
 def _quant_all(q, k, v, signs, block_rows):
