@@ -7,7 +7,10 @@ roundings of the bf16 path, each at most 2^-8 relative:
   * P rounded to bf16 before P.V: |error| <= 2^-8 (P|V|)_i.
   * O rounded to bf16 at the end: |error| <= 2^-8 |O|_i.
 So the bound is |o - o_ref| <= 2^-8 (|O| + P|V|) (1 + 1e-3) + 1e-5.  The gate
-also requires RMSE <= 5e-4 and LSE error <= 2e-4.  The oracle sees the same
+requires every element inside it, the RMS of error/bound <= 0.35 (a rounding
+error is rarely near its worst case), and the LSE error <= 2e-5.  One key
+masked wrongly moves the LSE by about p_j / sum p, so the LSE gate is
+sensitive to masking errors.  The oracle sees the same
 bf16-rounded inputs upcast to fp64, so the gate measures the kernel, not the
 input rounding.
 """
@@ -26,7 +29,7 @@ import exact_attention_74_amd as ea
 pytestmark = pytest.mark.gpu
 
 GATE_MAX, GATE_RMSE = 1e-2, 2e-3
-INT_RMSE, INT_LSE = 5e-4, 2e-4
+INT_NRMS, INT_LSE = 0.35, 2e-5
 U_BF16 = 2.0 ** -8
 
 
@@ -34,16 +37,17 @@ def _check(o, lse, o_ref, lse_ref, tag, o_absv=None):
     """o_absv: the oracle's attention applied to |V| (P|V|), for the rounding bound."""
     mx, rmse = err_stats(o, o_ref)
     lerr = float(np.abs(lse - lse_ref).max())
-    ratio = float("nan")
+    ratio = nrms = float("nan")
     if o_absv is not None:
         bound = U_BF16 * (np.abs(o_ref) + o_absv) * (1 + 1e-3) + 1e-5
-        ratio = float((np.abs(o - o_ref) / bound).max())
+        r = np.abs(o - o_ref) / bound
+        ratio, nrms = float(r.max()), float(np.sqrt(np.mean(r ** 2)))
     print(f"{tag}: max_abs={mx:.3e} rmse={rmse:.3e} lse_max={lerr:.3e} "
-          f"err/rounding_bound={ratio:.3f}", flush=True)
+          f"err/bound max={ratio:.3f} rms={nrms:.3f}", flush=True)
     assert mx <= GATE_MAX and rmse <= GATE_RMSE, (mx, rmse)
-    assert rmse <= INT_RMSE and lerr <= INT_LSE, (rmse, lerr)
+    assert lerr <= INT_LSE, lerr
     if o_absv is not None:
-        assert ratio <= 1.0, ratio
+        assert ratio <= 1.0 and nrms <= INT_NRMS, (ratio, nrms)
 
 
 def _run(dev_qkv, causal, scale):
@@ -176,7 +180,7 @@ def test_lse_none_and_stream():
     assert rc == 0
     o_ref, _ = oracle.naive_attention(*host, 0.125, False)
     mx, rmse = err_stats(to_np(o), o_ref)
-    assert mx <= GATE_MAX and rmse <= INT_RMSE
+    assert mx <= GATE_MAX and rmse <= GATE_RMSE
 
 
 def test_empty_problem_is_noop():
