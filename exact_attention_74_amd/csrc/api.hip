@@ -19,10 +19,14 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
   return pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
 }
 
-int check_shape(int B, int H, int N, int d) {
+// elt: bytes per element of the Q/K/V inputs.  One batch entry of a tensor
+// (N x H x d elements) must stay below 2 GiB: kernels address a head's rows
+// with 32-bit buffer offsets.
+int check_shape(int B, int H, int N, int d, int elt) {
   if (B < 0 || H < 0 || N < 0) return EXATTN_ERR_SHAPE;
   if (d != 64 && d != 128) return EXATTN_ERR_SHAPE;
   if ((int64_t)N >= kMaxN) return EXATTN_ERR_SHAPE;
+  if ((int64_t)N * H * d * elt >= (int64_t(1) << 31)) return EXATTN_ERR_SHAPE;
   const int64_t blocks = (int64_t)B * H * (((int64_t)N + 127) / 128);
   if (blocks >= (int64_t(1) << 31)) return EXATTN_ERR_SHAPE;
   return EXATTN_OK;
@@ -52,7 +56,7 @@ const char* exattn_strerror(int code) {
 
 int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                   int N, int d, int causal, float softmax_scale, void* stream) {
-  int rc = check_shape(B, H, N, d);
+  int rc = check_shape(B, H, N, d, 2);
   if (rc) return rc;
   if ((causal != 0 && causal != 1) || !good_scale(softmax_scale)) return EXATTN_ERR_VALUE;
   const int64_t bytes = (int64_t)B * N * H * d * 2;
@@ -71,7 +75,7 @@ int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* l
 int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_scale,
                  const float* k_scale, const float* v_scale, void* o, float* lse, int B, int H,
                  int N, int d, int causal, float softmax_scale, void* stream) {
-  int rc = check_shape(B, H, N, d);
+  int rc = check_shape(B, H, N, d, 1);
   if (rc) return rc;
   if ((causal != 0 && causal != 1) || !good_scale(softmax_scale)) return EXATTN_ERR_VALUE;
   const int64_t in_bytes = (int64_t)B * N * H * d;
@@ -93,7 +97,7 @@ int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_
 
 int blockquant_hadamard(const void* x, void* x8, float* scale, const float* signs, int B, int H,
                         int N, int d, int block_rows, void* stream) {
-  int rc = check_shape(B, H, N, d);
+  int rc = check_shape(B, H, N, d, 2);
   if (rc) return rc;
   if (block_rows != 0 && block_rows != 128) return EXATTN_ERR_VALUE;
   const int64_t n = (int64_t)B * N * H * d;

@@ -1,74 +1,159 @@
 // bf16 exact-attention forward for gfx950.
 //
 // Work decomposition (FA2 query-block parallelism, "Efficient Attention &
-// FlashAttention" M4-054): one workgroup per (b, h, block of 128 query rows),
-// four waves of 32 query rows each; the key/value sequence is streamed in
-// blocks of 64 keys through LDS with the online-softmax recurrence of the
-// FlashAttention-3 report, section 3 (running max m, running sum l, one final
-// normalisation).
+// FlashAttention" M4-054): one workgroup of 8 waves per (b, h, block of 256
+// query rows); each wave owns 32 query rows, two waves share a SIMD.  The
+// key/value sequence is streamed in blocks of 64 keys with the online-softmax
+// recurrence of the FlashAttention-3 report, section 3 (running max m,
+// running sum l, one final normalisation).
 //
 // Transposed formulation.  Each wave computes S^T = K Q^T (keys as MFMA rows,
-// its 32 queries as MFMA columns), so the accumulator puts every query on one
+// its 32 queries as MFMA columns), so the accumulator keeps every query on one
 // lane pair (l, l^32): row max and row sum are in-lane reductions plus one
 // cross-half exchange.  The output is accumulated as O^T = V^T P^T, whose
-// accumulator again keeps one query per lane, so the per-row rescale factor
-// is a lane-local scalar.  P^T is fed to the second MFMA straight from the S^T
-// accumulator registers (converted to bf16): with the accumulator layout, the
-// 8 k-slots of half-wave h in k-step t hold keys 16t + 8*(s/4) + 4h + s%4, and
-// V^T is stored in LDS with its keys permuted the same way (bits 2 and 3 of
-// the key index swapped within each group of 16), so no register shuffle is
-// needed.  This is the gfx950 counterpart of the report's accumulator-to-
-// operand relayout (section 3.3).
+// accumulator again keeps one query per lane, so the per-row rescale factor is
+// a lane-local scalar.  P^T goes to the second MFMA straight from the S^T
+// accumulator (converted to bf16): half-wave h, k-slot s of k-step t holds key
+// 16t + 8*(s/4) + 4h + s%4, and the V^T operand is gathered with the same key
+// order -- the gfx950 counterpart of the report's accumulator-to-operand
+// relayout (section 3.3).
+//
+// Memory pipeline (the report's producer/consumer overlap, section 3.1, done
+// the gfx950 way).  K and V tiles go from HBM/L2 straight into LDS with
+// buffer_load ... lds (no VGPR staging), two stages deep: the loads of tile
+// j+1 are in flight while tile j is consumed; one barrier per tile.  LDS rows
+// are XOR-swizzled in 16-byte chunks so that the ds_read_b128 of the K operand
+// and the ds_read_b64_tr_b16 transposed reads of the V operand are free of
+// bank conflicts; the V tile stays key-major in LDS and the transposed read
+// produces V^T fragments directly.  Reads past the end of the sequence come
+// back as zeros from the buffer descriptor's range check.
+//
+// Rescaling (exact, fewer non-matmul FLOPs, [FA-explain]).  A row's exp2
+// offset is raised to its block max only when that max exceeds the offset by
+// more than 8 (base 2); P is then at most 2^8 and O, l stay consistent with the
+// offset, so O / l and the LSE are unchanged while most blocks skip the O
+// rescale entirely.  The decision is per row, so a row's arithmetic depends on
+// its own visible keys only.
 #include "common.h"
 #include "launch.h"
 
 namespace exattn {
 namespace {
 
-constexpr int kBR = 128;  // query rows per workgroup
-constexpr int kBC = 64;   // keys per KV block
-constexpr int kThreads = 256;
+constexpr int kBR = 256;     // query rows per workgroup
+constexpr int kBC = 64;      // keys per KV block
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr float kLazy = 8.f;  // rescale threshold (log2 units)
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+template <int D>
+struct Geo {
+  static constexpr int RB = 2 * D;           // bytes per key row
+  static constexpr int CPR = D / 8;          // 16-byte chunks per row
+  static constexpr int RP = 256 / RB;        // rows per 256-byte bank cycle
+  static constexpr int TILE = kBC * RB;      // bytes per K or V tile
+  static constexpr int STAGE = 2 * TILE;     // K + V
+  static constexpr int LOADS = TILE / (1024 * kWaves);  // 1 KB loads per wave per tile
+  // chunk position of chunk c of row `row`
+  __device__ static int swz_k(int row) { return (row / RP) % CPR; }
+  __device__ static int swz_v(int row) { return 4 * ((row / RP) % (CPR / 4)); }
+};
+
+// Asynchronous 16-byte-per-lane copy global -> LDS; lane i's chunk lands at
+// lds_dst + 16 i (lds_dst is wave-uniform).
+__device__ __forceinline__ void copy_to_lds16(__amdgpu_buffer_rsrc_t r, char* lds_dst,
+                                              uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 16, voff, soff, 0, 0);
+}
+
+__device__ __forceinline__ bf16x4 read_tr16(const char* lds_generic_base, int byte_off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4*)((__attribute__((address_space(3))) char*)lds_generic_base + byte_off));
+}
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    __bf16* __restrict__ O, float* __restrict__ LSE, int H, int N, float scale_log2, int nqb) {
-  constexpr int KP = D + 8;    // K tile row pitch (elements); +16 B breaks bank aliasing
-  constexpr int VP = kBC + 8;  // V^T tile row pitch (elements)
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[kBC * KP];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[D * VP];
+    __bf16* __restrict__ O, float* __restrict__ LSE, int H, int N, float scale_log2, int nqb,
+    int xcd_remap) {
+  using G = Geo<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * G::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int li = lane & 31;  // query column of this lane
-  const int hh = lane >> 5;  // half-wave
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  const int li = lane & 31;
+  const int hh = lane >> 5;
 
-  const int bid = blockIdx.x;
-  const int qb_raw = bid % nqb;
-  const int bh = bid / nqb;  // b * H + h
+  int L = blockIdx.x;
+  if (xcd_remap) L = (L & 7) * (gridDim.x >> 3) + (L >> 3);  // one head's q-blocks per XCD
+  const int qb_raw = L % nqb;
+  const int bh = L / nqb;
   const int qblk = CAUSAL ? (nqb - 1 - qb_raw) : qb_raw;  // heaviest causal blocks first
   const int b = bh / H;
   const int h = bh - b * H;
-  const int64_t rs = (int64_t)H * D;  // element stride between sequence positions
+  const int64_t rs = (int64_t)H * D;
   const int64_t head_off = ((int64_t)b * N * H + h) * D;
-  const __bf16* Qh = Q + head_off;
-  const __bf16* Kh = K + head_off;
-  const __bf16* Vh = V + head_off;
 
-  const int q0 = qblk * kBR + wave * 32;  // first query row of this wave
-  const int qi = q0 + li;                 // this lane's query row
+  const int q0 = qblk * kBR + wave * 32;
+  const int qi = q0 + li;
 
-  // Q^T as the B operand: k-step t covers head dims 16t .. 16t+15, half h
-  // holds dims 16t + 8h .. +7 of query qi.
+  // Q^T as the B operand: k-step t, half h -> dims 16t + 8h .. +7 of query qi.
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) {
     bf16x8 z = {};
-    qf[t] = (qi < N) ? *(const bf16x8*)(Qh + (int64_t)qi * rs + 16 * t + 8 * hh) : z;
+    qf[t] = (qi < N) ? *(const bf16x8*)(Q + head_off + (int64_t)qi * rs + 16 * t + 8 * hh) : z;
   }
 
-  float m = kNoMax;  // running max of scale*log2(e)*s (base-2 domain)
+  // Buffer descriptors over this head's K and V rows; row n >= N is out of
+  // range (reads return 0).
+  const uint32_t nbytes = (uint32_t)(((int64_t)(N - 1) * rs + D) * 2);
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(K + head_off), (short)0, nbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(V + head_off), (short)0, nbytes, 0x00020000);
+  const uint32_t row_bytes = (uint32_t)(rs * 2);
+
+  // Per-lane global byte offsets of the chunks this lane deposits into LDS.
+  uint32_t voff_k[G::LOADS], voff_v[G::LOADS];
+#pragma unroll
+  for (int i = 0; i < G::LOADS; ++i) {
+    const int chunk = (wave * G::LOADS + i) * 64 + lane;  // LDS chunk slot within a tile
+    const int row = chunk / G::CPR, pos = chunk % G::CPR;
+    voff_k[i] = row * row_bytes + (uint32_t)((pos ^ G::swz_k(row)) * 16);
+    voff_v[i] = row * row_bytes + (uint32_t)((pos ^ G::swz_v(row)) * 16);
+  }
+#define LOAD_TILE(stage, k0)                                                                    \
+  do {                                                                                          \
+    const uint32_t soff_ = (uint32_t)(k0) * row_bytes;                                          \
+    _Pragma("unroll") for (int i_ = 0; i_ < G::LOADS; ++i_) {                                   \
+      char* dst_ = smem + (stage) * G::STAGE + (wave * G::LOADS + i_) * 1024;                   \
+      copy_to_lds16(rk, dst_, voff_k[i_], soff_);                                               \
+      copy_to_lds16(rv, dst_ + G::TILE, voff_v[i_], soff_);                                     \
+    }                                                                                           \
+  } while (0)
+
+  // LDS byte offsets (within a tile) of this lane's operand fragments.
+  int kaddr[D / 16];  // K rows li (+32 for the second block), chunk 2t + hh
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) kaddr[t] = li * G::RB + (((2 * t + hh) ^ G::swz_k(li)) * 16);
+  int vaddr[D / 32];  // transposed-read source: key 4h + j, dims 32e + 16(g%2) + 4q
+  {
+    const int src = lane & 15, g = lane >> 4;
+    const int j = src >> 2, q = src & 3, hv = g >> 1;
+    const int row = 4 * hv + j;
+#pragma unroll
+    for (int e = 0; e < D / 32; ++e) {
+      const int c = 4 * e + 2 * (g & 1) + (q >> 1);
+      vaddr[e] = row * G::RB + ((c ^ G::swz_v(row)) * 16) + (q & 1) * 8;
+    }
+  }
+
+  float m = kNoMax;  // exp2 offset (base-2 domain), raised lazily
   float l = 0.f;     // running sum over this lane's half of the keys
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -77,62 +162,33 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(
   const int nkb_all = ceil_div(N, kBC);
   const int nkb = CAUSAL ? min(nkb_all, ceil_div(min(N, (qblk + 1) * kBR), kBC)) : nkb_all;
 
+  LOAD_TILE(0, 0);
   for (int kb = 0; kb < nkb; ++kb) {
     const int k0 = kb * kBC;
-    __syncthreads();  // previous tiles fully consumed
-    // K tile, row-major, 16-byte chunks.
-#pragma unroll
-    for (int c = tid; c < kBC * D / 8; c += kThreads) {
-      const int r = c / (D / 8), cc = c % (D / 8);
-      bf16x8 val = {};
-      if (k0 + r < N) val = *(const bf16x8*)(Kh + (int64_t)(k0 + r) * rs + cc * 8);
-      *(bf16x8*)(Ks + r * KP + cc * 8) = val;
-    }
-    // V tile, transposed to V^T[d][key'] with key' = key with bits 2,3 swapped
-    // inside each group of 16.  A unit is 8 keys x 8 dims: keys
-    // {4hb..4hb+3, 8+4hb..8+4hb+3} of one 16-group land contiguously at
-    // positions 8hb..8hb+7.
-#pragma unroll
-    for (int c = tid; c < (kBC / 16) * 2 * (D / 8); c += kThreads) {
-      const int dc = c % (D / 8);
-      const int hb = (c / (D / 8)) & 1;
-      const int g16 = c / (D / 4);
-      i32x4 r[8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int key = k0 + g16 * 16 + (s < 4 ? 4 * hb + s : 8 + 4 * hb + (s - 4));
-        i32x4 z = {};
-        r[s] = (key < N) ? *(const i32x4*)(Vh + (int64_t)key * rs + dc * 8) : z;
-      }
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const int w = dd >> 1;
-        const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
-        i32x4 out;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          out[u] = (int)__builtin_amdgcn_perm((uint32_t)r[2 * u + 1][w], (uint32_t)r[2 * u][w], sel);
-        *(i32x4*)(Vt + (dc * 8 + dd) * VP + g16 * 16 + 8 * hb) = out;
-      }
-    }
-    __syncthreads();
+    const int stage = kb & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // tile kb resident; every wave is done with the other stage
+    if (kb + 1 < nkb) LOAD_TILE(stage ^ 1, k0 + kBC);
+    if (CAUSAL && k0 > q0 + 31) continue;  // every key of this tile is after this wave's rows
 
-    // S^T = K Q^T for the 64 keys, as two 32x32 accumulators.
-    f32x16 sacc[kBC / 32];
+    const char* kt = smem + stage * G::STAGE;
+    const char* vt = kt + G::TILE;
+
+    // S^T = K Q^T: two 32-key blocks.
+    f32x16 sacc[2];
 #pragma unroll
-    for (int j = 0; j < kBC / 32; ++j) {
+    for (int j = 0; j < 2; ++j) {
       sacc[j] = f32x16{};
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) {
-        const bf16x8 a = *(const bf16x8*)(Ks + (j * 32 + li) * KP + 16 * t + 8 * hh);
+        const bf16x8 a = *(const bf16x8*)(kt + kaddr[t] + j * 32 * G::RB);
         sacc[j] = mfma_bf16(a, qf[t], sacc[j]);
       }
     }
 
-    // Mask keys past the end and (causal) keys after the query.
     if (k0 + kBC > N || (CAUSAL && k0 + kBC - 1 > q0)) {
 #pragma unroll
-      for (int j = 0; j < kBC / 32; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = k0 + j * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
@@ -140,47 +196,48 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(
         }
     }
 
-    // Online softmax in the base-2 domain.
-    float mx = -INFINITY;
+    float mx = fmaxf(sacc[0][0], sacc[0][1]);
 #pragma unroll
-    for (int j = 0; j < kBC / 32; ++j)
+    for (int v = 2; v < 16; v += 2) mx = fmaxf(mx, fmaxf(sacc[0][v], sacc[0][v + 1]));
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[j][v]);
+    for (int v = 0; v < 16; v += 2) mx = fmaxf(mx, fmaxf(sacc[1][v], sacc[1][v + 1]));
     mx = fmaxf(mx, xor32(mx));
-    const float m_new = fmaxf(m, mx * scale_log2);
-    const float alpha = exp2_fast(m - m_new);
+    const float mb = mx * scale_log2;
+    const bool raise = mb > m + kLazy;  // per row: each row's offset depends on its own keys only
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      const float m_new = raise ? mb : m;
+      const float alpha = exp2_fast(m - m_new);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int e = 0; e < D / 32; ++e) oacc[e] *= alpha;
+    }
+    const float neg_m = -m;
     float rsum = 0.f;
+    bf16x8 pb[4];
 #pragma unroll
-    for (int j = 0; j < kBC / 32; ++j)
+    for (int t2 = 0; t2 < 4; ++t2)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = exp2_fast(__builtin_fmaf(sacc[j][v], scale_log2, -m_new));
-        sacc[j][v] = p;
+      for (int s = 0; s < 8; ++s) {
+        const float p = exp2_fast(__builtin_fmaf(sacc[t2 >> 1][8 * (t2 & 1) + s], scale_log2, neg_m));
         rsum += p;
+        pb[t2][s] = (__bf16)p;
       }
-    l = l * alpha + rsum;
-    m = m_new;
-#pragma unroll
-    for (int e = 0; e < D / 32; ++e) oacc[e] *= alpha;
+    l += rsum;
 
-    // P^T (bf16) as the B operand: k-step t2 takes accumulator registers
-    // 8*(t2%2) .. +7 of block t2/2.
-    bf16x8 pb[kBC / 16];
-#pragma unroll
-    for (int t2 = 0; t2 < kBC / 16; ++t2)
-#pragma unroll
-      for (int s = 0; s < 8; ++s) pb[t2][s] = (__bf16)sacc[t2 >> 1][8 * (t2 & 1) + s];
-
-    // O^T += V^T P^T.
+    // O^T += V^T P^T; the V^T fragment of k-step t2 is two transposed reads.
 #pragma unroll
     for (int e = 0; e < D / 32; ++e)
 #pragma unroll
-      for (int t2 = 0; t2 < kBC / 16; ++t2) {
-        const bf16x8 a = *(const bf16x8*)(Vt + (32 * e + li) * VP + 16 * t2 + 8 * hh);
+      for (int t2 = 0; t2 < 4; ++t2) {
+        const bf16x4 lo = read_tr16(vt, vaddr[e] + (16 * t2) * G::RB);
+        const bf16x4 hi = read_tr16(vt, vaddr[e] + (16 * t2 + 8) * G::RB);
+        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         oacc[e] = mfma_bf16(a, pb[t2], oacc[e]);
       }
   }
 
+#undef LOAD_TILE
   // Epilogue: one normalisation per row, bf16 store, log-sum-exp.
   const float lt = l + xor32(l);
   const float inv = 1.f / lt;
@@ -203,10 +260,11 @@ template <int D, bool CAUSAL>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                   int N, float scale, hipStream_t stream) {
   const int nqb = (N + kBR - 1) / kBR;
-  const unsigned grid = (unsigned)((int64_t)B * H * nqb);
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, stream,
-                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, H, N,
-                     scale * kLog2e, nqb);
+  const int64_t grid = (int64_t)B * H * nqb;
+  const int remap = (grid % 8 == 0) ? 1 : 0;
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0,
+                     stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse,
+                     H, N, scale * kLog2e, nqb, remap);
   return hipGetLastError();
 }
 

@@ -24,7 +24,9 @@
  *               the sizes and values are valid; pointers may then be NULL);
  *               d in {64, 128} (other head dims are zero-padded by the caller
  *               to 64 or 128, keeping softmax_scale = 1/sqrt(d_original); the
- *               same blog, section 3.1); B*H*ceil(N/128) < 2^31; N < 2^24.
+ *               same blog, section 3.1); B*H*ceil(N/128) < 2^31; N < 2^24;
+ *               N*H*d*(bytes per input element) < 2^31 (one batch entry of
+ *               a tensor below 2 GiB: rows are addressed with 32-bit offsets).
  *   Memory      every pointer is device memory owned by the caller; the
  *               library allocates and frees nothing and keeps no state
  *               between calls.  Tensor pointers must be 16-byte aligned

@@ -78,6 +78,7 @@ def test_attention_validation(fn):
     assert fn(B=-3) == ea.ERR_SHAPE
     assert fn(N=1 << 24) == ea.ERR_SHAPE
     assert fn(B=1 << 20, H=1 << 10, N=1 << 16) == ea.ERR_SHAPE
+    assert fn(H=1 << 12, N=1 << 16, d=128) == ea.ERR_SHAPE  # one batch entry >= 2 GiB
     assert fn(scale=0.0) == ea.ERR_VALUE
     assert fn(scale=-1.0) == ea.ERR_VALUE
     assert fn(scale=float("inf")) == ea.ERR_VALUE
