@@ -26,14 +26,16 @@
 // and the ds_read_b64_tr_b16 transposed reads of the V operand are free of
 // bank conflicts; the V tile stays key-major in LDS and the transposed read
 // produces V^T fragments directly.  Reads past the end of the sequence come
-// back as zeros from the buffer descriptor's range check.
+// back as zeros from the buffer descriptor's range check.  Within a tile, all
+// K fragments are read before the S MFMAs, and all V^T fragments before the
+// softmax, whose VALU work then covers their LDS latency.
 //
-// Rescaling (exact, fewer non-matmul FLOPs, [FA-explain]).  A row's exp2
-// offset is raised to its block max only when that max exceeds the offset by
-// more than 8 (base 2); P is then at most 2^8 and O, l stay consistent with the
-// offset, so O / l and the LSE are unchanged while most blocks skip the O
-// rescale entirely.  The decision is per row, so a row's arithmetic depends on
-// its own visible keys only.
+// Rescaling (exact, fewer non-matmul FLOPs: "Efficient Attention &
+// FlashAttention", FA2 section).  A row's exp2 offset is raised to its block
+// max only when that max exceeds the offset by more than 8 (base 2); P is then
+// at most 2^8 and O, l stay consistent with the offset, so O / l and the LSE
+// are unchanged while most blocks skip the O rescale entirely.  The decision
+// is per row, so a row's arithmetic depends on its own visible keys only.
 #include "common.h"
 #include "launch.h"
 
@@ -174,17 +176,29 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
     const char* kt = smem + stage * G::STAGE;
     const char* vt = kt + G::TILE;
 
-    // S^T = K Q^T: two 32-key blocks.
+    // S^T = K Q^T: two 32-key blocks.  All K fragments are read first.
+    bf16x8 kf[2][D / 16];
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) kf[j][t] = *(const bf16x8*)(kt + kaddr[t] + j * 32 * G::RB);
     f32x16 sacc[2];
+    sacc[0] = sacc[1] = f32x16{};
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      sacc[j] = f32x16{};
+    for (int t = 0; t < D / 16; ++t)
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-        const bf16x8 a = *(const bf16x8*)(kt + kaddr[t] + j * 32 * G::RB);
-        sacc[j] = mfma_bf16(a, qf[t], sacc[j]);
+      for (int j = 0; j < 2; ++j) sacc[j] = mfma_bf16(kf[j][t], qf[t], sacc[j]);
+    // V^T fragments for this tile's P.V, read before the softmax so that the
+    // exp/sum work covers their latency.
+    bf16x8 vf[4][D / 32];
+#pragma unroll
+    for (int t2 = 0; t2 < 4; ++t2)
+#pragma unroll
+      for (int e = 0; e < D / 32; ++e) {
+        const bf16x4 lo = read_tr16(vt, vaddr[e] + (16 * t2) * G::RB);
+        const bf16x4 hi = read_tr16(vt, vaddr[e] + (16 * t2 + 8) * G::RB);
+        vf[t2][e] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
-    }
 
     if (k0 + kBC > N || (CAUSAL && k0 + kBC - 1 > q0)) {
 #pragma unroll
@@ -225,16 +239,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
       }
     l += rsum;
 
-    // O^T += V^T P^T; the V^T fragment of k-step t2 is two transposed reads.
+    // O^T += V^T P^T.
 #pragma unroll
-    for (int e = 0; e < D / 32; ++e)
+    for (int t2 = 0; t2 < 4; ++t2)
 #pragma unroll
-      for (int t2 = 0; t2 < 4; ++t2) {
-        const bf16x4 lo = read_tr16(vt, vaddr[e] + (16 * t2) * G::RB);
-        const bf16x4 hi = read_tr16(vt, vaddr[e] + (16 * t2 + 8) * G::RB);
-        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        oacc[e] = mfma_bf16(a, pb[t2], oacc[e]);
-      }
+      for (int e = 0; e < D / 32; ++e) oacc[e] = mfma_bf16(vf[t2][e], pb[t2], oacc[e]);
   }
 
 #undef LOAD_TILE
