@@ -1,81 +1,113 @@
-// FP8 (OCP e4m3) exact-attention forward for gfx950, the low-precision scheme
-// of the FlashAttention-3 report, section 3.3.
+// FP8 (OCP e4m3) exact-attention forward for gfx950: the low-precision scheme
+// of the FlashAttention-3 report, section 3.3, on v_mfma_f32_32x32x64_f8f6f4.
 //
-// Same decomposition as the bf16 kernel (one workgroup per (b, h, 128 query
-// rows), four waves of 32 rows, transposed S^T = K Q^T / O^T = V^T P^T
-// formulation) with 128-key blocks, so that every query block and every key
-// block coincides with one 128-row quantisation block:
+// Decomposition as in the bf16 kernel: one workgroup of 8 waves per (b, h,
+// block of 256 query rows), 32 query rows per wave, two waves per SIMD; the
+// keys are streamed 128 at a time, so every key tile is exactly one
+// quantisation block and every wave's rows lie in one query block:
 //   * S block scaling: the tile's scalar q_scale * k_scale * softmax_scale *
 //     log2(e) multiplies the fp32 accumulator inside the exp2 argument.
+//   * Transposed formulation S^T = K Q^T and O^T = V^T P^T: every query sits
+//     on one lane pair, so row max / row sum are in-lane plus one exchange.
 //   * P is rounded to e4m3 (v_cvt_pk_fp8_f32) straight from the S^T
 //     accumulator: half-wave h, byte slot s of the 64-key k-step u holds key
 //     64u + 32*(s/16) + 8*((s%16)/4) + 4h + s%4.
-//   * In-LDS V relayout: the fp8 MFMA wants, per lane, 32 consecutive k bytes
-//     of one head dim, so the V tile is written to LDS transposed (V^T, key
-//     bytes contiguous) with its keys permuted to match the slot order above.
-//     Each unit of 16 keys x 16 dims is a 16x16 byte transpose in registers.
-//   * V block scales: O is kept in units of the current block's v_scale and
-//     rescaled by alpha * v_scale_prev / v_scale_cur when the block changes.
+//   * V relayout in LDS: the V tile stays key-major in LDS and each lane's
+//     32-key V^T operand is gathered with four ds_read_b64_tr_b8 transposed
+//     reads in exactly the slot order above (the gfx950 counterpart of the
+//     report's in-kernel V transpose and byte permute).
+//   * V block scales: O is kept in units of the current tile's v_scale and
+//     rescaled by alpha * v_scale_prev / v_scale_cur at each tile, together
+//     with the online-softmax correction alpha.  The running max follows the
+//     report's recurrence exactly (raised at every tile).
+// K and V tiles go from HBM/L2 straight into XOR-swizzled LDS with
+// buffer_load ... lds, two stages deep, one barrier per tile; reads past the
+// end of the sequence return zeros.
 #include "common.h"
 #include "launch.h"
 
 namespace exattn {
 namespace {
 
-constexpr int kBR = 128;
-constexpr int kBC = 128;
+constexpr int kBR = 256;
+constexpr int kBC = 128;  // keys per tile = rows per quantisation block
 constexpr int kQB = 128;  // rows per quantisation block
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 
-// 16x16 byte transpose: out[j] byte i = in[i] byte j.
-__device__ __forceinline__ void transpose16x16(const i32x4 (&in)[16], i32x4 (&out)[16]) {
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int w = j >> 2, sh = 8 * (j & 3);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t v = 0;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) v |= (((uint32_t)in[4 * q + t][w] >> sh) & 0xFFu) << (8 * t);
-      out[j][q] = (int)v;
-    }
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+template <int D>
+struct Geo8 {
+  static constexpr int RB = D;                // bytes per key row
+  static constexpr int CPR = D / 16;          // 16-byte chunks per row
+  static constexpr int RP = 256 / RB;         // rows per 256-byte bank cycle
+  static constexpr int TILE = kBC * RB;       // bytes per K or V tile
+  static constexpr int STAGE = 2 * TILE;      // K + V
+  static constexpr int LOADS = TILE / (1024 * kWaves);
+  // chunk c of row `row` is stored at chunk position c ^ swz(row)
+  __device__ static int swz_k(int row) { return (row / RP) % CPR; }
+  __device__ static int swz_v(int row) {
+    if (D == 128) return 2 * (((row >> 1) & 1) | (((row >> 3) & 1) << 1));
+    return 2 * ((row >> 3) & 1);
   }
+};
+
+__device__ __forceinline__ void copy_to_lds16(__amdgpu_buffer_rsrc_t r, char* lds_dst,
+                                              uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 16, voff, soff, 0, 0);
+}
+
+__device__ __forceinline__ i32x2 read_tr8(const char* lds_generic_base, int byte_off) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (lds_i32x2*)((__attribute__((address_space(3))) char*)lds_generic_base + byte_off));
+}
+
+// -inf for keys >= N and, when causal, keys after query qi.  k0: first key.
+__device__ __forceinline__ void mask_s8(f32x16 (&sacc)[4], int k0, int N, bool causal, int qi,
+                                        int hh) {
+  const int lim = causal ? min(N, qi + 1) : N;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int key = k0 + j * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+      if (key >= lim) sacc[j][v] = -INFINITY;
+    }
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
     const float* __restrict__ SQ, const float* __restrict__ SK, const float* __restrict__ SV,
-    __bf16* __restrict__ O, float* __restrict__ LSE, int H, int N, float scale_log2, int nqb) {
-  constexpr int KP = D + 16;    // bytes
-  constexpr int VP = kBC + 16;  // bytes
-  __shared__ __attribute__((aligned(16))) uint8_t Ks[kBC * KP];
-  __shared__ __attribute__((aligned(16))) uint8_t Vt[D * VP];
+    __bf16* __restrict__ O, float* __restrict__ LSE, int H, int N, float scale_log2, int nqb,
+    int xcd_remap) {
+  using G = Geo8<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * G::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31;
   const int hh = lane >> 5;
 
-  const int bid = blockIdx.x;
-  const int qb_raw = bid % nqb;
-  const int bh = bid / nqb;
+  int L = blockIdx.x;
+  if (xcd_remap) L = (L & 7) * (gridDim.x >> 3) + (L >> 3);
+  const int qb_raw = L % nqb;
+  const int bh = L / nqb;
   const int qblk = CAUSAL ? (nqb - 1 - qb_raw) : qb_raw;
   const int b = bh / H;
   const int h = bh - b * H;
   const int64_t rs = (int64_t)H * D;
   const int64_t head_off = ((int64_t)b * N * H + h) * D;
-  const uint8_t* Qh = Q + head_off;
-  const uint8_t* Kh = K + head_off;
-  const uint8_t* Vh = V + head_off;
   const int nsb = (N + kQB - 1) / kQB;
   const float* sk_bh = SK + (int64_t)bh * nsb;
   const float* sv_bh = SV + (int64_t)bh * nsb;
-  const float sq = SQ[(int64_t)bh * nsb + qblk];
 
   const int q0 = qblk * kBR + wave * 32;
   const int qi = q0 + li;
+  const float sq = (q0 < N) ? SQ[(int64_t)bh * nsb + q0 / kQB] : 0.f;
 
   // Q^T as the B operand: k-step t covers dims 64t .. 64t+63; half h holds
   // dims 64t + 32h .. +31 of query qi.
@@ -83,7 +115,52 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(
 #pragma unroll
   for (int t = 0; t < D / 64; ++t) {
     i32x8 z = {};
-    qf[t] = (qi < N) ? *(const i32x8*)(Qh + (int64_t)qi * rs + 64 * t + 32 * hh) : z;
+    qf[t] = (qi < N) ? *(const i32x8*)(Q + head_off + (int64_t)qi * rs + 64 * t + 32 * hh) : z;
+  }
+
+  const uint32_t nbytes = (uint32_t)((int64_t)(N - 1) * rs + D);
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(K + head_off), (short)0, nbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(V + head_off), (short)0, nbytes, 0x00020000);
+  const uint32_t row_bytes = (uint32_t)rs;
+  uint32_t voff_k[G::LOADS], voff_v[G::LOADS];
+#pragma unroll
+  for (int i = 0; i < G::LOADS; ++i) {
+    const int chunk = (wave * G::LOADS + i) * 64 + lane;
+    const int row = chunk / G::CPR, pos = chunk % G::CPR;
+    voff_k[i] = row * row_bytes + (uint32_t)((pos ^ G::swz_k(row)) * 16);
+    voff_v[i] = row * row_bytes + (uint32_t)((pos ^ G::swz_v(row)) * 16);
+  }
+#define LOAD_TILE(stage, k0)                                                                    \
+  do {                                                                                          \
+    const uint32_t soff_ = (uint32_t)(k0) * row_bytes;                                          \
+    _Pragma("unroll") for (int i_ = 0; i_ < G::LOADS; ++i_) {                                   \
+      char* dst_ = smem + (stage) * G::STAGE + (wave * G::LOADS + i_) * 1024;                   \
+      copy_to_lds16(rk, dst_, voff_k[i_], soff_);                                               \
+      copy_to_lds16(rv, dst_ + G::TILE, voff_v[i_], soff_);                                     \
+    }                                                                                           \
+  } while (0)
+
+  // K operand: row li, 16-byte chunks 4t + 2hh and 4t + 2hh + 1.
+  int kaddr[D / 64][2];
+#pragma unroll
+  for (int t = 0; t < D / 64; ++t)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      kaddr[t][c] = li * G::RB + (((4 * t + 2 * hh + c) ^ G::swz_k(li)) * 16);
+  // V^T operand, transposed read r of k-step u: source lane 2j + q of group g
+  // points at key 64u + 16r + 8(j/4) + 4(g/2) + j%4, dims 32e + 16(g%2) + 8q.
+  int vaddr[D / 32];
+  {
+    const int src = lane & 15, g = lane >> 4;
+    const int j = src >> 1, q = src & 1;
+    const int kl = 8 * (j >> 2) + 4 * (g >> 1) + (j & 3);
+#pragma unroll
+    for (int e = 0; e < D / 32; ++e) {
+      const int c = 2 * e + (g & 1);
+      vaddr[e] = kl * G::RB + ((c ^ G::swz_v(kl)) * 16) + 8 * q;
+    }
   }
 
   float m = kNoMax;
@@ -94,108 +171,99 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(
   for (int e = 0; e < D / 32; ++e) oacc[e] = f32x16{};
 
   const int nkb_all = ceil_div(N, kBC);
-  const int nkb = CAUSAL ? min(nkb_all, qblk + 1) : nkb_all;
+  const int nkb = CAUSAL ? min(nkb_all, ceil_div(min(N, (qblk + 1) * kBR), kBC)) : nkb_all;
 
+  LOAD_TILE(0, 0);
   for (int kb = 0; kb < nkb; ++kb) {
     const int k0 = kb * kBC;
+    const int stage = kb & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-#pragma unroll
-    for (int c = tid; c < kBC * D / 16; c += kThreads) {
-      const int r = c / (D / 16), cc = c % (D / 16);
-      i32x4 val = {};
-      if (k0 + r < N) val = *(const i32x4*)(Kh + (int64_t)(k0 + r) * rs + cc * 16);
-      *(i32x4*)(Ks + r * KP + cc * 16) = val;
-    }
-    // V^T relayout.  Unit (u, hv, c2, dc): keys 64u + 32c2 + 8g + 4hv + r
-    // (g, r in 0..3) x dims 16dc .. 16dc+15, written to V^T rows
-    // 16dc .. +15 at byte positions 64u + 32hv + 16c2 + 4g + r.
-#pragma unroll
-    for (int c = tid; c < (kBC / 64) * 4 * (D / 16); c += kThreads) {
-      const int dc = c % (D / 16);
-      const int c2 = (c / (D / 16)) & 1;
-      const int hv = (c / (D / 8)) & 1;
-      const int u = c / (D / 4);
-      i32x4 in[16], out[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int key = k0 + 64 * u + 32 * c2 + 8 * (j >> 2) + 4 * hv + (j & 3);
-        i32x4 z = {};
-        in[j] = (key < N) ? *(const i32x4*)(Vh + (int64_t)key * rs + dc * 16) : z;
-      }
-      transpose16x16(in, out);
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        *(i32x4*)(Vt + (16 * dc + j) * VP + 64 * u + 32 * hv + 16 * c2) = out[j];
-    }
-    __syncthreads();
+    if (kb + 1 < nkb) LOAD_TILE(stage ^ 1, k0 + kBC);
+    if (CAUSAL && k0 > q0 + 31) continue;
 
-    f32x16 sacc[kBC / 32];
-#pragma unroll
-    for (int j = 0; j < kBC / 32; ++j) {
-      sacc[j] = f32x16{};
-#pragma unroll
-      for (int t = 0; t < D / 64; ++t) {
-        const i32x8 a = *(const i32x8*)(Ks + (j * 32 + li) * KP + 64 * t + 32 * hh);
-        sacc[j] = mfma_fp8(a, qf[t], sacc[j]);
-      }
-    }
+    const char* kt = smem + stage * G::STAGE;
+    const char* vt = kt + G::TILE;
 
-    if (k0 + kBC > N || (CAUSAL && k0 + kBC - 1 > q0)) {
+    // S^T = K Q^T: four 32-key blocks; all K fragments are read first.
+    i32x8 kf[4][D / 64];
 #pragma unroll
-      for (int j = 0; j < kBC / 32; ++j)
+    for (int t = 0; t < D / 64; ++t)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = k0 + j * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-          if (key >= N || (CAUSAL && key > qi)) sacc[j][v] = -INFINITY;
-        }
-    }
+      for (int j = 0; j < 4; ++j) {
+        const i32x4 lo = *(const i32x4*)(kt + kaddr[t][0] + j * 32 * G::RB);
+        const i32x4 hi = *(const i32x4*)(kt + kaddr[t][1] + j * 32 * G::RB);
+        kf[j][t] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+    f32x16 sacc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sacc[j] = f32x16{};
+#pragma unroll
+    for (int t = 0; t < D / 64; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sacc[j] = mfma_fp8(kf[j][t], qf[t], sacc[j]);
+
+    // V^T fragments for this tile's P.V, read before the softmax.
+    i32x8 vf[2][D / 32];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < D / 32; ++e) {
+        i32x2 r[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) r[rr] = read_tr8(vt, vaddr[e] + (64 * u + 16 * rr) * G::RB);
+        vf[u][e] = i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
+      }
+
+    if (k0 + kBC > N || (CAUSAL && k0 + kBC - 1 > q0)) mask_s8(sacc, k0, N, CAUSAL, qi, hh);
 
     const float c_tile = scale_log2 * sq * sk_bh[kb];
     const float sv = sv_bh[kb];
-    float mx = -INFINITY;
+    float mx0 = fmaxf(sacc[0][0], sacc[0][1]), mx1 = fmaxf(sacc[2][0], sacc[2][1]);
 #pragma unroll
-    for (int j = 0; j < kBC / 32; ++j)
+    for (int v = 2; v < 16; v += 2) {
+      mx0 = fmaxf(mx0, fmaxf(sacc[0][v], sacc[0][v + 1]));
+      mx1 = fmaxf(mx1, fmaxf(sacc[2][v], sacc[2][v + 1]));
+    }
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[j][v]);
+    for (int v = 0; v < 16; v += 2) {
+      mx0 = fmaxf(mx0, fmaxf(sacc[1][v], sacc[1][v + 1]));
+      mx1 = fmaxf(mx1, fmaxf(sacc[3][v], sacc[3][v + 1]));
+    }
+    float mx = fmaxf(mx0, mx1);
     mx = fmaxf(mx, xor32(mx));
     const float m_new = fmaxf(m, mx * c_tile);
     const float alpha = exp2_fast(m - m_new);
+    m = m_new;
+    const float neg_m = -m;
     float rsum = 0.f;
+    i32x8 pf[2];
 #pragma unroll
-    for (int j = 0; j < kBC / 32; ++j)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = exp2_fast(__builtin_fmaf(sacc[j][v], c_tile, -m_new));
-        sacc[j][v] = p;
-        rsum += p;
+      for (int w = 0; w < 8; ++w) {
+        const f32x16& sa = sacc[2 * u + (w >> 2)];
+        const int r0 = 4 * (w & 3);
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[i] = exp2_fast(__builtin_fmaf(sa[r0 + i], c_tile, neg_m));
+          rsum += p[i];
+        }
+        pf[u][w] = (int)pack_fp8x4(p[0], p[1], p[2], p[3]);
       }
     l = l * alpha + rsum;
-    m = m_new;
     const float f = alpha * (sv_prev / sv);
     sv_prev = sv;
 #pragma unroll
     for (int e = 0; e < D / 32; ++e) oacc[e] *= f;
 
-    // P^T in e4m3: k-step u, word w holds slots 4w..4w+3 = accumulator
-    // block 2u + w/4, registers 4(w%4) .. +3.
-    i32x8 pf[kBC / 64];
 #pragma unroll
-    for (int u = 0; u < kBC / 64; ++u)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const f32x16& sa = sacc[2 * u + (w >> 2)];
-        const int r0 = 4 * (w & 3);
-        pf[u][w] = (int)pack_fp8x4(sa[r0], sa[r0 + 1], sa[r0 + 2], sa[r0 + 3]);
-      }
-
-#pragma unroll
-    for (int e = 0; e < D / 32; ++e)
-#pragma unroll
-      for (int u = 0; u < kBC / 64; ++u) {
-        const i32x8 a = *(const i32x8*)(Vt + (32 * e + li) * VP + 64 * u + 32 * hh);
-        oacc[e] = mfma_fp8(a, pf[u], oacc[e]);
-      }
+      for (int e = 0; e < D / 32; ++e) oacc[e] = mfma_fp8(vf[u][e], pf[u], oacc[e]);
   }
+#undef LOAD_TILE
 
   const float lt = l + xor32(l);
   const float inv = sv_prev / lt;
@@ -219,10 +287,11 @@ hipError_t launch(const void* q8, const void* k8, const void* v8, const float* s
                   const float* sv, void* o, float* lse, int B, int H, int N, float scale,
                   hipStream_t stream) {
   const int nqb = (N + kBR - 1) / kBR;
-  const unsigned grid = (unsigned)((int64_t)B * H * nqb);
-  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, stream,
-                     (const uint8_t*)q8, (const uint8_t*)k8, (const uint8_t*)v8, sq, sk, sv,
-                     (__bf16*)o, lse, H, N, scale * kLog2e, nqb);
+  const int64_t grid = (int64_t)B * H * nqb;
+  const int remap = (grid % 8 == 0) ? 1 : 0;
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0,
+                     stream, (const uint8_t*)q8, (const uint8_t*)k8, (const uint8_t*)v8, sq, sk, sv,
+                     (__bf16*)o, lse, H, N, scale * kLog2e, nqb, remap);
   return hipGetLastError();
 }
 
