@@ -3,13 +3,14 @@
 // with block quantisation to OCP e4m3.
 //
 // HBM-bound: one read of the bf16 tensor and one write of the e4m3 codes.  A
-// workgroup owns one 128-row x d block of one (b, h); d/8 lanes share a row,
-// each lane holding 8 consecutive elements, so a row is read and written with
-// 16-byte (bf16) and 8-byte (e4m3) vector accesses.  The fast Walsh-Hadamard
-// transform runs its butterfly strides 1, 2, 4 inside the lane and strides
-// 8 .. d/2 across lanes (xor-shuffles within the row's lane group); every
-// butterfly is one fp32 add or subtract, in increasing-stride order.  The
-// block's amax is reduced across the workgroup, then the codes are
+// workgroup owns one 128-row x d block of one (b, h); 4 lanes share a row and
+// lane r holds the 8-element chunks r, r+4, ..., so each load instruction of
+// a row's lanes covers 64 contiguous bytes.  The fast Walsh-Hadamard
+// transform runs butterfly strides 1, 2, 4 inside each chunk, 8 and 16 across
+// the row's 4 lanes (DPP quad permutes, no LDS traffic) and 32, 64 across the
+// lane's chunks; every butterfly is one fp32 add or subtract, in
+// increasing-stride order.  The block's amax is
+// reduced across the workgroup, then the codes are
 // e4m3_rne(y * fp32(448 / amax)).
 #include "common.h"
 #include "launch.h"
@@ -22,13 +23,23 @@ constexpr int kThreads = 256;
 
 enum Mode { kQuantBlock = 0, kAmaxOnly = 1, kQuantGiven = 2 };
 
+// Cross-lane butterfly partner within a group of 4 lanes (DPP quad_perm):
+// xor 1 -> [1,0,3,2], xor 2 -> [2,3,0,1].
+template <int XOR>
+__device__ __forceinline__ float quad_xor(float v) {
+  constexpr int ctrl = (XOR == 1) ? 0xB1 : 0x4E;
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xF,
+                                                            0xF, true));
+}
+
 template <int D, bool ROTATE, int MODE>
 __global__ __launch_bounds__(kThreads) void blockquant_kernel(const __bf16* __restrict__ X,
                                                               uint8_t* __restrict__ X8,
                                                               float* __restrict__ S,
                                                               const float* __restrict__ signs,
                                                               int H, int N, int nsb, float kconst) {
-  constexpr int LPR = D / 8;             // lanes per row
+  constexpr int LPR = 4;                 // lanes per row
+  constexpr int EPL = D / LPR;           // elements per lane (32 or 16)
   constexpr int RPP = kThreads / LPR;    // rows per pass
   constexpr int PASSES = kRows / RPP;
   __shared__ float red[kThreads / 64];
@@ -44,48 +55,82 @@ __global__ __launch_bounds__(kThreads) void blockquant_kernel(const __bf16* __re
   const int64_t rs = (int64_t)H * D;
   const int64_t head_off = ((int64_t)b * N * H + h) * D;
 
-  float sg[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) sg[e] = ROTATE ? signs[lr * 8 + e] : 1.f;
-
-  float y[PASSES][8];
-  float amax = 0.f;
+  // Lane lr of a row holds the 8-element chunks lr, lr+4, lr+8, ... (element
+  // 32c + 8lr + k is y[.][c][k]), so the row's 4 lanes read 64 contiguous
+  // bytes per load instruction.
+  constexpr int NC = EPL / 8;  // chunks per lane
+  float y[PASSES][NC][8];
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int row = sb * kRows + p * RPP + rsub;
-    bf16x8 xv = {};
-    if (row < N) xv = *(const bf16x8*)(X + head_off + (int64_t)row * rs + lr * 8);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[p][e] = (float)xv[e];
-    if (ROTATE) {
+    for (int c = 0; c < NC; ++c) {
+      bf16x8 xv = {};
+      if (row < N) xv = *(const bf16x8*)(X + head_off + (int64_t)row * rs + 32 * c + 8 * lr);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) y[p][e] *= sg[e];
-      // strides 1, 2, 4 inside the lane
-#pragma unroll
-      for (int st = 1; st < 8; st <<= 1) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if ((e & st) == 0) {
-            const float a = y[p][e], c = y[p][e + st];
-            y[p][e] = a + c;
-            y[p][e + st] = a - c;
-          }
-        }
-      }
-      // strides 8 .. D/2 across the lanes of the row
-#pragma unroll
-      for (int lm = 1; lm < LPR; lm <<= 1) {
-        const bool upper = (lr & lm) != 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float other = __shfl_xor(y[p][e], lm, 64);
-          y[p][e] = upper ? (other - y[p][e]) : (y[p][e] + other);
-        }
-      }
+      for (int k = 0; k < 8; ++k) y[p][c][k] = (float)xv[k];
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(y[p][e]));
   }
+  float amax = 0.f;
+  if (ROTATE) {
+    float sg[NC][8];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sg[c][k] = signs[32 * c + 8 * lr + k];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) y[p][c][k] *= sg[c][k];
+      // strides 1, 2, 4: inside each chunk
+#pragma unroll
+      for (int st = 1; st < 8; st <<= 1)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if ((k & st) == 0) {
+              const float a = y[p][c][k], b2 = y[p][c][k + st];
+              y[p][c][k] = a + b2;
+              y[p][c][k + st] = a - b2;
+            }
+      // strides 8, 16: across the row's 4 lanes
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float o = quad_xor<1>(y[p][c][k]);
+          y[p][c][k] = (lr & 1) ? (o - y[p][c][k]) : (y[p][c][k] + o);
+        }
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float o = quad_xor<2>(y[p][c][k]);
+          y[p][c][k] = (lr & 2) ? (o - y[p][c][k]) : (y[p][c][k] + o);
+        }
+      // strides 32, 64: across this lane's chunks
+#pragma unroll
+      for (int st = 1; st < NC; st <<= 1)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          if ((c & st) == 0)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              const float a = y[p][c][k], b2 = y[p][c + st][k];
+              y[p][c][k] = a + b2;
+              y[p][c + st][k] = a - b2;
+            }
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(y[p][c][k]));
 
   // workgroup max
 #pragma unroll
@@ -116,10 +161,13 @@ __global__ __launch_bounds__(kThreads) void blockquant_kernel(const __bf16* __re
   for (int p = 0; p < PASSES; ++p) {
     const int row = sb * kRows + p * RPP + rsub;
     if (row < N) {
-      i32x2 c;
-      c[0] = (int)pack_fp8x4(y[p][0] * r, y[p][1] * r, y[p][2] * r, y[p][3] * r);
-      c[1] = (int)pack_fp8x4(y[p][4] * r, y[p][5] * r, y[p][6] * r, y[p][7] * r);
-      *(i32x2*)(X8 + head_off + (int64_t)row * rs + lr * 8) = c;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        i32x2 w;
+        w[0] = (int)pack_fp8x4(y[p][c][0] * r, y[p][c][1] * r, y[p][c][2] * r, y[p][c][3] * r);
+        w[1] = (int)pack_fp8x4(y[p][c][4] * r, y[p][c][5] * r, y[p][c][6] * r, y[p][c][7] * r);
+        *(i32x2*)(X8 + head_off + (int64_t)row * rs + 32 * c + 8 * lr) = w;
+      }
     }
   }
   if (tid == 0) S[bid] = scale;
