@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+CALIB_COPY_BYTES = 256 << 20
 
 
 def parse():
@@ -41,7 +42,32 @@ def parse():
     p.add_argument("--B", type=int, default=4)
     p.add_argument("--H", type=int, default=16)
     p.add_argument("--d", type=int, default=128)
+    p.add_argument("--calib-copy", action="store_true",
+                   help="also run one plain 256 MiB device copy (untimed), the reference that "
+                        "scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
     return p.parse_args()
+
+
+def profiled_traffic(kernel: str, workload: str):
+    """HBM bytes per launch (read + write) from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, or None when that summary is for another
+    workload or the kernel's sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    k = rec.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    h = hashlib.sha256()
+    for src in k["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != k["sha256"]:
+        return None
+    return k["read_bytes"] + k["write_bytes"]
 
 
 def cpu_baseline(w, target_s: float):
@@ -135,6 +161,14 @@ def main():
             if evs is not None:
                 evs[i][1].record(stream)
 
+    if a.calib_copy:
+        src = torch.empty(CALIB_COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     print(f"[bench] workload {w16.name}: warmup {a.warmup}", file=sys.stderr, flush=True)
     for _ in range(a.warmup):
         step()
@@ -190,7 +224,9 @@ def main():
         "kernel_ms_median": {n: round(v, 4) for n, v in med.items()},
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_bf16", "achieved": round(tf16, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tf16 / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(tf16 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": profiled_traffic("attn_fwd_bf16", f"attn_fwd_b{B}h{H}n{N}d{d}"
+                                                 if not a.causal else "none"),
                      "algorithmic_flops_per_launch": flops},
         "outputs_finite": ok,
     }
