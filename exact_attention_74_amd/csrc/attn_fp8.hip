@@ -173,97 +173,106 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   const int nkb_all = ceil_div(N, kBC);
   const int nkb = CAUSAL ? min(nkb_all, ceil_div(min(N, (qblk + 1) * kBR), kBC)) : nkb_all;
 
+  // Interior tiles (no key past the end, no key after any of the workgroup's
+  // query rows) run a copy of the tile body without masking; the few edge
+  // tiles at the end run the masked copy.
+#define TILE_BODY(MASKED)                                                                            \
+    const int k0 = kb * kBC;                                                                         \
+    const int stage = kb & 1;                                                                        \
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                                 \
+    __syncthreads();                                                                                 \
+    if (kb + 1 < nkb) LOAD_TILE(stage ^ 1, k0 + kBC);                                                \
+    if (CAUSAL && k0 > q0 + 31) continue; /* this and later tiles are after the wave's rows */       \
+                                                                                                     \
+    const char* kt = smem + stage * G::STAGE;                                                        \
+    const char* vt = kt + G::TILE;                                                                   \
+                                                                                                     \
+    i32x8 kf[4][D / 64];                                                                             \
+_Pragma("unroll")                                                                                    \
+    for (int t = 0; t < D / 64; ++t)                                                                 \
+_Pragma("unroll")                                                                                    \
+      for (int j = 0; j < 4; ++j) {                                                                  \
+        const i32x4 lo = *(const i32x4*)(kt + kaddr[t][0] + j * 32 * G::RB);                         \
+        const i32x4 hi = *(const i32x4*)(kt + kaddr[t][1] + j * 32 * G::RB);                         \
+        kf[j][t] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};                    \
+      }                                                                                              \
+    f32x16 sacc[4];                                                                                  \
+_Pragma("unroll")                                                                                    \
+    for (int j = 0; j < 4; ++j) sacc[j] = f32x16{};                                                  \
+_Pragma("unroll")                                                                                    \
+    for (int t = 0; t < D / 64; ++t)                                                                 \
+_Pragma("unroll")                                                                                    \
+      for (int j = 0; j < 4; ++j) sacc[j] = mfma_fp8(kf[j][t], qf[t], sacc[j]);                      \
+                                                                                                     \
+    if (MASKED) mask_s8(sacc, k0, N, CAUSAL, qi, hh);                                                \
+                                                                                                     \
+    const float c_tile = scale_log2 * sq * sk_bh[kb];                                                \
+    const float sv = sv_bh[kb];                                                                      \
+    float mx0 = fmaxf(sacc[0][0], sacc[0][1]), mx1 = fmaxf(sacc[2][0], sacc[2][1]);                  \
+_Pragma("unroll")                                                                                    \
+    for (int v = 2; v < 16; v += 2) {                                                                \
+      mx0 = fmaxf(mx0, fmaxf(sacc[0][v], sacc[0][v + 1]));                                           \
+      mx1 = fmaxf(mx1, fmaxf(sacc[2][v], sacc[2][v + 1]));                                           \
+    }                                                                                                \
+_Pragma("unroll")                                                                                    \
+    for (int v = 0; v < 16; v += 2) {                                                                \
+      mx0 = fmaxf(mx0, fmaxf(sacc[1][v], sacc[1][v + 1]));                                           \
+      mx1 = fmaxf(mx1, fmaxf(sacc[3][v], sacc[3][v + 1]));                                           \
+    }                                                                                                \
+    float mx = fmaxf(mx0, mx1);                                                                      \
+    mx = fmaxf(mx, xor32(mx));                                                                       \
+    const float m_new = fmaxf(m, mx * c_tile);                                                       \
+    const float alpha = exp2_fast(m - m_new);                                                        \
+    m = m_new;                                                                                       \
+    const float neg_m = -m;                                                                          \
+    float rsum = 0.f;                                                                                \
+    i32x8 pf[2];                                                                                     \
+_Pragma("unroll")                                                                                    \
+    for (int u = 0; u < 2; ++u)                                                                      \
+_Pragma("unroll")                                                                                    \
+      for (int w = 0; w < 8; ++w) {                                                                  \
+        const f32x16& sa = sacc[2 * u + (w >> 2)];                                                   \
+        const int r0 = 4 * (w & 3);                                                                  \
+        float p[4];                                                                                  \
+_Pragma("unroll")                                                                                    \
+        for (int i = 0; i < 4; ++i) {                                                                \
+          p[i] = exp2_fast(__builtin_fmaf(sa[r0 + i], c_tile, neg_m));                               \
+          rsum += p[i];                                                                              \
+        }                                                                                            \
+        pf[u][w] = (int)pack_fp8x4(p[0], p[1], p[2], p[3]);                                          \
+      }                                                                                              \
+    l = l * alpha + rsum;                                                                            \
+    const float f = alpha * (sv_prev / sv);                                                          \
+    sv_prev = sv;                                                                                    \
+_Pragma("unroll")                                                                                    \
+    for (int e = 0; e < D / 32; ++e) oacc[e] *= f;                                                   \
+                                                                                                     \
+    i32x8 vf[2][D / 32];                                                                             \
+_Pragma("unroll")                                                                                    \
+    for (int u = 0; u < 2; ++u)                                                                      \
+_Pragma("unroll")                                                                                    \
+      for (int e = 0; e < D / 32; ++e) {                                                             \
+        i32x2 r[4];                                                                                  \
+_Pragma("unroll")                                                                                    \
+        for (int rr = 0; rr < 4; ++rr) r[rr] = read_tr8(vt, vaddr[e] + (64 * u + 16 * rr) * G::RB);  \
+        vf[u][e] = i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};    \
+      }                                                                                              \
+                                                                                                     \
+_Pragma("unroll")                                                                                    \
+    for (int u = 0; u < 2; ++u)                                                                      \
+_Pragma("unroll")                                                                                    \
+      for (int e = 0; e < D / 32; ++e) oacc[e] = mfma_fp8(vf[u][e], pf[u], oacc[e]);                 \
+
+  const int nkb_int = min(nkb, min(CAUSAL ? qblk * (kBR / kBC) : nkb, N / kBC));
   LOAD_TILE(0, 0);
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int k0 = kb * kBC;
-    const int stage = kb & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kb + 1 < nkb) LOAD_TILE(stage ^ 1, k0 + kBC);
-    if (CAUSAL && k0 > q0 + 31) continue;
-
-    const char* kt = smem + stage * G::STAGE;
-    const char* vt = kt + G::TILE;
-
-    // S^T = K Q^T: four 32-key blocks; all K fragments are read first.
-    i32x8 kf[4][D / 64];
-#pragma unroll
-    for (int t = 0; t < D / 64; ++t)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const i32x4 lo = *(const i32x4*)(kt + kaddr[t][0] + j * 32 * G::RB);
-        const i32x4 hi = *(const i32x4*)(kt + kaddr[t][1] + j * 32 * G::RB);
-        kf[j][t] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-    f32x16 sacc[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sacc[j] = f32x16{};
-#pragma unroll
-    for (int t = 0; t < D / 64; ++t)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sacc[j] = mfma_fp8(kf[j][t], qf[t], sacc[j]);
-
-    // V^T fragments for this tile's P.V, read before the softmax.
-    i32x8 vf[2][D / 32];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int e = 0; e < D / 32; ++e) {
-        i32x2 r[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) r[rr] = read_tr8(vt, vaddr[e] + (64 * u + 16 * rr) * G::RB);
-        vf[u][e] = i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
-      }
-
-    if (k0 + kBC > N || (CAUSAL && k0 + kBC - 1 > q0)) mask_s8(sacc, k0, N, CAUSAL, qi, hh);
-
-    const float c_tile = scale_log2 * sq * sk_bh[kb];
-    const float sv = sv_bh[kb];
-    float mx0 = fmaxf(sacc[0][0], sacc[0][1]), mx1 = fmaxf(sacc[2][0], sacc[2][1]);
-#pragma unroll
-    for (int v = 2; v < 16; v += 2) {
-      mx0 = fmaxf(mx0, fmaxf(sacc[0][v], sacc[0][v + 1]));
-      mx1 = fmaxf(mx1, fmaxf(sacc[2][v], sacc[2][v + 1]));
-    }
-#pragma unroll
-    for (int v = 0; v < 16; v += 2) {
-      mx0 = fmaxf(mx0, fmaxf(sacc[1][v], sacc[1][v + 1]));
-      mx1 = fmaxf(mx1, fmaxf(sacc[3][v], sacc[3][v + 1]));
-    }
-    float mx = fmaxf(mx0, mx1);
-    mx = fmaxf(mx, xor32(mx));
-    const float m_new = fmaxf(m, mx * c_tile);
-    const float alpha = exp2_fast(m - m_new);
-    m = m_new;
-    const float neg_m = -m;
-    float rsum = 0.f;
-    i32x8 pf[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const f32x16& sa = sacc[2 * u + (w >> 2)];
-        const int r0 = 4 * (w & 3);
-        float p[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[i] = exp2_fast(__builtin_fmaf(sa[r0 + i], c_tile, neg_m));
-          rsum += p[i];
-        }
-        pf[u][w] = (int)pack_fp8x4(p[0], p[1], p[2], p[3]);
-      }
-    l = l * alpha + rsum;
-    const float f = alpha * (sv_prev / sv);
-    sv_prev = sv;
-#pragma unroll
-    for (int e = 0; e < D / 32; ++e) oacc[e] *= f;
-
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int e = 0; e < D / 32; ++e) oacc[e] = mfma_fp8(vf[u][e], pf[u], oacc[e]);
+  for (int kb = 0; kb < nkb_int; ++kb) {
+    TILE_BODY(false);
+  }
+  for (int kb = nkb_int; kb < nkb; ++kb) {
+    TILE_BODY(true);
   }
 #undef LOAD_TILE
+#undef TILE_BODY
 
   const float lt = l + xor32(l);
   const float inv = sv_prev / lt;
