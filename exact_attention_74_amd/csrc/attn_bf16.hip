@@ -76,6 +76,97 @@ __device__ __forceinline__ bf16x4 read_tr16(const char* lds_generic_base, int by
       (lds_bf16x4*)((__attribute__((address_space(3))) char*)lds_generic_base + byte_off));
 }
 
+
+// -inf for keys >= N and, when causal, keys after query qi.  k0: first key.
+__device__ __forceinline__ void mask_s(f32x16 (&sacc)[2], int k0, int N, bool causal, int qi,
+                                       int hh) {
+  const int lim = causal ? min(N, qi + 1) : N;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int key = k0 + j * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+      if (key >= lim) sacc[j][v] = -INFINITY;
+    }
+}
+
+// In-lane max over this lane's 32 scores (the other half-wave holds the rest).
+__device__ __forceinline__ float rowmax(const f32x16 (&s)[2]) {
+  float a = fmaxf(s[0][0], s[0][1]), b = fmaxf(s[1][0], s[1][1]);
+#pragma unroll
+  for (int v = 2; v < 16; v += 2) {
+    a = fmaxf(a, fmaxf(s[0][v], s[0][v + 1]));
+    b = fmaxf(b, fmaxf(s[1][v], s[1][v + 1]));
+  }
+  return fmaxf(a, b);
+}
+
+// One key tile: S^T = K Q^T, (masking,) online softmax with lazy offset, and
+// O^T += V^T P^T.  kt: the tile's K buffer in LDS; its V buffer follows.
+template <int D, bool CAUSAL, bool MASKED>
+__device__ __forceinline__ void tile_compute(const char* kt, const int (&kaddr)[D / 16],
+                                             const int (&vaddr)[D / 32], const bf16x8 (&qf)[D / 16],
+                                             f32x16 (&oacc)[D / 32], float& m, float& l, int k0,
+                                             int N, int qi, int hh, float scale_log2) {
+  using G = Geo<D>;
+  const char* vt = kt + G::TILE;
+  // S^T = K Q^T: two 32-key blocks.  All K fragments are read first.
+  bf16x8 kf[2][D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) kf[j][t] = *(const bf16x8*)(kt + kaddr[t] + j * 32 * G::RB);
+  f32x16 sacc[2];
+  sacc[0] = sacc[1] = f32x16{};
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) sacc[j] = mfma_bf16(kf[j][t], qf[t], sacc[j]);
+  // V^T fragments for this tile's P.V, read before the softmax so that the
+  // exp/sum work covers their latency.
+  bf16x8 vf[4][D / 32];
+#pragma unroll
+  for (int t2 = 0; t2 < 4; ++t2)
+#pragma unroll
+    for (int e = 0; e < D / 32; ++e) {
+      const bf16x4 lo = read_tr16(vt, vaddr[e] + (16 * t2) * G::RB);
+      const bf16x4 hi = read_tr16(vt, vaddr[e] + (16 * t2 + 8) * G::RB);
+      vf[t2][e] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  if (MASKED) mask_s(sacc, k0, N, CAUSAL, qi, hh);
+
+  float mx = rowmax(sacc);
+  mx = fmaxf(mx, xor32(mx));
+  const float mb = mx * scale_log2;
+  const bool raise = mb > m + kLazy;  // per row: each row's offset depends on its own keys only
+  if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+    const float m_new = raise ? mb : m;
+    const float alpha = exp2_fast(m - m_new);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < D / 32; ++e) oacc[e] *= alpha;
+  }
+  const float neg_m = -m;
+  float rsum = 0.f;
+  bf16x8 pb[4];
+#pragma unroll
+  for (int t2 = 0; t2 < 4; ++t2)
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const float p = exp2_fast(__builtin_fmaf(sacc[t2 >> 1][8 * (t2 & 1) + s], scale_log2, neg_m));
+      rsum += p;
+      pb[t2][s] = (__bf16)p;
+    }
+  l += rsum;
+
+  // O^T += V^T P^T.
+#pragma unroll
+  for (int t2 = 0; t2 < 4; ++t2)
+#pragma unroll
+    for (int e = 0; e < D / 32; ++e) oacc[e] = mfma_bf16(vf[t2][e], pb[t2], oacc[e]);
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
@@ -164,87 +255,32 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
   const int nkb_all = ceil_div(N, kBC);
   const int nkb = CAUSAL ? min(nkb_all, ceil_div(min(N, (qblk + 1) * kBR), kBC)) : nkb_all;
 
+  // Interior tiles (no key past the end, no key after any row of this
+  // workgroup) need no masking and come first; they run two at a time so the
+  // LDS stage of each is a compile-time constant.  The few edge tiles follow.
+  const int nkb_int = min(nkb, CAUSAL ? qblk * (kBR / kBC) : N / kBC);
+#define STEP(ST_, KB, MASKED)                                                                    \
+  do {                                                                                          \
+    const int kb_ = (KB);                                                                       \
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                           \
+    __syncthreads(); /* tile kb_ resident; every wave is done with the other stage */           \
+    if (kb_ + 1 < nkb) LOAD_TILE((ST_) ^ 1, (kb_ + 1) * kBC);                                   \
+    if (!(CAUSAL && kb_ * kBC > q0 + 31))                                                       \
+      tile_compute<D, CAUSAL, MASKED>(smem + (ST_) * G::STAGE, kaddr, vaddr, qf, oacc, m, l,     \
+                                      kb_ * kBC, N, qi, hh, scale_log2);                        \
+  } while (0)
   LOAD_TILE(0, 0);
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int k0 = kb * kBC;
-    const int stage = kb & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // tile kb resident; every wave is done with the other stage
-    if (kb + 1 < nkb) LOAD_TILE(stage ^ 1, k0 + kBC);
-    if (CAUSAL && k0 > q0 + 31) continue;  // every key of this tile is after this wave's rows
-
-    const char* kt = smem + stage * G::STAGE;
-    const char* vt = kt + G::TILE;
-
-    // S^T = K Q^T: two 32-key blocks.  All K fragments are read first.
-    bf16x8 kf[2][D / 16];
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) kf[j][t] = *(const bf16x8*)(kt + kaddr[t] + j * 32 * G::RB);
-    f32x16 sacc[2];
-    sacc[0] = sacc[1] = f32x16{};
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) sacc[j] = mfma_bf16(kf[j][t], qf[t], sacc[j]);
-    // V^T fragments for this tile's P.V, read before the softmax so that the
-    // exp/sum work covers their latency.
-    bf16x8 vf[4][D / 32];
-#pragma unroll
-    for (int t2 = 0; t2 < 4; ++t2)
-#pragma unroll
-      for (int e = 0; e < D / 32; ++e) {
-        const bf16x4 lo = read_tr16(vt, vaddr[e] + (16 * t2) * G::RB);
-        const bf16x4 hi = read_tr16(vt, vaddr[e] + (16 * t2 + 8) * G::RB);
-        vf[t2][e] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-
-    if (k0 + kBC > N || (CAUSAL && k0 + kBC - 1 > q0)) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = k0 + j * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-          if (key >= N || (CAUSAL && key > qi)) sacc[j][v] = -INFINITY;
-        }
-    }
-
-    float mx = fmaxf(sacc[0][0], sacc[0][1]);
-#pragma unroll
-    for (int v = 2; v < 16; v += 2) mx = fmaxf(mx, fmaxf(sacc[0][v], sacc[0][v + 1]));
-#pragma unroll
-    for (int v = 0; v < 16; v += 2) mx = fmaxf(mx, fmaxf(sacc[1][v], sacc[1][v + 1]));
-    mx = fmaxf(mx, xor32(mx));
-    const float mb = mx * scale_log2;
-    const bool raise = mb > m + kLazy;  // per row: each row's offset depends on its own keys only
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-      const float m_new = raise ? mb : m;
-      const float alpha = exp2_fast(m - m_new);
-      m = m_new;
-      l *= alpha;
-#pragma unroll
-      for (int e = 0; e < D / 32; ++e) oacc[e] *= alpha;
-    }
-    const float neg_m = -m;
-    float rsum = 0.f;
-    bf16x8 pb[4];
-#pragma unroll
-    for (int t2 = 0; t2 < 4; ++t2)
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const float p = exp2_fast(__builtin_fmaf(sacc[t2 >> 1][8 * (t2 & 1) + s], scale_log2, neg_m));
-        rsum += p;
-        pb[t2][s] = (__bf16)p;
-      }
-    l += rsum;
-
-    // O^T += V^T P^T.
-#pragma unroll
-    for (int t2 = 0; t2 < 4; ++t2)
-#pragma unroll
-      for (int e = 0; e < D / 32; ++e) oacc[e] = mfma_bf16(vf[t2][e], pb[t2], oacc[e]);
+  int kb = 0;
+  for (; kb + 1 < nkb_int; kb += 2) {
+    STEP(0, kb, false);
+    STEP(1, kb + 1, false);
   }
+  if (kb < nkb_int) {
+    STEP(0, kb, false);
+    ++kb;
+  }
+  for (; kb < nkb; ++kb) STEP(kb & 1, kb, true);
+#undef STEP
 
 #undef LOAD_TILE
   // Epilogue: one normalisation per row, bf16 store, log-sum-exp.
