@@ -49,7 +49,6 @@ constexpr int kThreads = 64 * kWaves;
 constexpr float kLazy = 8.f;  // rescale threshold (log2 units)
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 template <int D>
 struct Geo {
@@ -71,9 +70,39 @@ __device__ __forceinline__ void copy_to_lds16(__amdgpu_buffer_rsrc_t r, char* ld
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 16, voff, soff, 0, 0);
 }
 
-__device__ __forceinline__ bf16x4 read_tr16(const char* lds_generic_base, int byte_off) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (lds_bf16x4*)((__attribute__((address_space(3))) char*)lds_generic_base + byte_off));
+// LDS byte address of a generic pointer into LDS.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Transposed LDS read (ds_read_b64_tr_b16) at LDS address addr + OFF, issued
+// as assembly.  With the builtin, the compiler's wait-count pass assumes the
+// read may see LDS that an in-flight buffer_load ... lds is writing and drains
+// vmcnt first, which ties the next tile's prefetch to this tile's V reads; the
+// tile loop's own vmcnt wait and barrier already order the two.  The result is
+// valid only after lds_wait_v() has taken it.
+template <int OFF>
+__device__ __forceinline__ bf16x4 read_tr16(uint32_t addr) {
+  bf16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+// Waits for every outstanding LDS read, passing the V^T fragments through so
+// that no use of them is scheduled before the wait.
+template <int NE>
+__device__ __forceinline__ void lds_wait_v(bf16x8 (&vf)[4][NE]) {
+  static_assert(NE == 4 || NE == 2, "d = 128 or 64");
+  if constexpr (NE == 4)
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(vf[0][0]), "+v"(vf[0][1]), "+v"(vf[0][2]), "+v"(vf[0][3]),
+                   "+v"(vf[1][0]), "+v"(vf[1][1]), "+v"(vf[1][2]), "+v"(vf[1][3]),
+                   "+v"(vf[2][0]), "+v"(vf[2][1]), "+v"(vf[2][2]), "+v"(vf[2][3]),
+                   "+v"(vf[3][0]), "+v"(vf[3][1]), "+v"(vf[3][2]), "+v"(vf[3][3]));
+  else
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(vf[0][0]), "+v"(vf[0][1]), "+v"(vf[1][0]), "+v"(vf[1][1]),
+                   "+v"(vf[2][0]), "+v"(vf[2][1]), "+v"(vf[3][0]), "+v"(vf[3][1]));
 }
 
 
@@ -101,15 +130,17 @@ __device__ __forceinline__ float rowmax(const f32x16 (&s)[2]) {
   return fmaxf(a, b);
 }
 
-// One key tile: S^T = K Q^T, (masking,) online softmax with lazy offset, and
-// O^T += V^T P^T.  kt: the tile's K buffer in LDS; its V buffer follows.
-template <int D, bool CAUSAL, bool MASKED>
-__device__ __forceinline__ void tile_compute(const char* kt, const int (&kaddr)[D / 16],
-                                             const int (&vaddr)[D / 32], const bf16x8 (&qf)[D / 16],
-                                             f32x16 (&oacc)[D / 32], float& m, float& l, int k0,
-                                             int N, int qi, int hh, float scale_log2) {
+// One key tile in LDS stage ST: S^T = K Q^T, (masking,) online softmax with
+// lazy offset, and O^T += V^T P^T.  smem: the LDS tile buffers; vaddr: LDS
+// addresses of this lane's V^T fragment sources in stage 0's V buffer.
+template <int D, bool CAUSAL, bool MASKED, int ST>
+__device__ __forceinline__ void tile_compute(const char* smem, const int (&kaddr)[D / 16],
+                                             const uint32_t (&vaddr)[D / 32],
+                                             const bf16x8 (&qf)[D / 16], f32x16 (&oacc)[D / 32],
+                                             float& m, float& l, int k0, int N, int qi, int hh,
+                                             float scale_log2) {
   using G = Geo<D>;
-  const char* vt = kt + G::TILE;
+  const char* kt = smem + ST * G::STAGE;
   // S^T = K Q^T: two 32-key blocks.  All K fragments are read first.
   bf16x8 kf[2][D / 16];
 #pragma unroll
@@ -125,18 +156,21 @@ __device__ __forceinline__ void tile_compute(const char* kt, const int (&kaddr)[
   // V^T fragments for this tile's P.V, read before the softmax so that the
   // exp/sum work covers their latency.
   bf16x8 vf[4][D / 32];
+  constexpr int VOFF = ST * G::STAGE + G::TILE;
 #pragma unroll
-  for (int t2 = 0; t2 < 4; ++t2)
-#pragma unroll
-    for (int e = 0; e < D / 32; ++e) {
-      const bf16x4 lo = read_tr16(vt, vaddr[e] + (16 * t2) * G::RB);
-      const bf16x4 hi = read_tr16(vt, vaddr[e] + (16 * t2 + 8) * G::RB);
-      vf[t2][e] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
+  for (int e = 0; e < D / 32; ++e) {
+#define TR_PAIR(T2)                                                                              \
+  {                                                                                              \
+    const bf16x4 lo = read_tr16<VOFF + (16 * (T2)) * G::RB>(vaddr[e]);                          \
+    const bf16x4 hi = read_tr16<VOFF + (16 * (T2) + 8) * G::RB>(vaddr[e]);                      \
+    vf[T2][e] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};                  \
+  }
+    TR_PAIR(0) TR_PAIR(1) TR_PAIR(2) TR_PAIR(3)
+#undef TR_PAIR
+  }
   if (MASKED) mask_s(sacc, k0, N, CAUSAL, qi, hh);
 
-  float mx = rowmax(sacc);
-  mx = fmaxf(mx, xor32(mx));
+  const float mx = max_halves(rowmax(sacc));
   const float mb = mx * scale_log2;
   const bool raise = mb > m + kLazy;  // per row: each row's offset depends on its own keys only
   if (__builtin_amdgcn_ballot_w64(raise) != 0) {
@@ -161,6 +195,7 @@ __device__ __forceinline__ void tile_compute(const char* kt, const int (&kaddr)[
   l += rsum;
 
   // O^T += V^T P^T.
+  lds_wait_v(vf);
 #pragma unroll
   for (int t2 = 0; t2 < 4; ++t2)
 #pragma unroll
@@ -234,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
   int kaddr[D / 16];  // K rows li (+32 for the second block), chunk 2t + hh
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) kaddr[t] = li * G::RB + (((2 * t + hh) ^ G::swz_k(li)) * 16);
-  int vaddr[D / 32];  // transposed-read source: key 4h + j, dims 32e + 16(g%2) + 4q
+  uint32_t vaddr[D / 32];  // transposed-read source: key 4h + j, dims 32e + 16(g%2) + 4q
   {
     const int src = lane & 15, g = lane >> 4;
     const int j = src >> 2, q = src & 3, hv = g >> 1;
@@ -242,7 +277,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int e = 0; e < D / 32; ++e) {
       const int c = 4 * e + 2 * (g & 1) + (q >> 1);
-      vaddr[e] = row * G::RB + ((c ^ G::swz_v(row)) * 16) + (q & 1) * 8;
+      vaddr[e] = lds_addr(smem) + row * G::RB + ((c ^ G::swz_v(row)) * 16) + (q & 1) * 8;
     }
   }
 
@@ -256,9 +291,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
   const int nkb = CAUSAL ? min(nkb_all, ceil_div(min(N, (qblk + 1) * kBR), kBC)) : nkb_all;
 
   // Interior tiles (no key past the end, no key after any row of this
-  // workgroup) need no masking and come first; they run two at a time so the
-  // LDS stage of each is a compile-time constant.  The few edge tiles follow.
-  const int nkb_int = min(nkb, CAUSAL ? qblk * (kBR / kBC) : N / kBC);
+  // workgroup) need no masking and come first; the few edge tiles follow.
+  // Both loops take tiles two at a time from an even tile index, so the LDS
+  // stage of every step is a compile-time constant.
+  const int nkb_int = min(nkb, CAUSAL ? qblk * (kBR / kBC) : N / kBC) & ~1;
 #define STEP(ST_, KB, MASKED)                                                                    \
   do {                                                                                          \
     const int kb_ = (KB);                                                                       \
@@ -266,25 +302,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
     __syncthreads(); /* tile kb_ resident; every wave is done with the other stage */           \
     if (kb_ + 1 < nkb) LOAD_TILE((ST_) ^ 1, (kb_ + 1) * kBC);                                   \
     if (!(CAUSAL && kb_ * kBC > q0 + 31))                                                       \
-      tile_compute<D, CAUSAL, MASKED>(smem + (ST_) * G::STAGE, kaddr, vaddr, qf, oacc, m, l,     \
-                                      kb_ * kBC, N, qi, hh, scale_log2);                        \
+      tile_compute<D, CAUSAL, MASKED, ST_>(smem, kaddr, vaddr, qf, oacc, m, l, kb_ * kBC, N, qi, \
+                                           hh, scale_log2);                                     \
   } while (0)
   LOAD_TILE(0, 0);
   int kb = 0;
-  for (; kb + 1 < nkb_int; kb += 2) {
+  for (; kb < nkb_int; kb += 2) {
     STEP(0, kb, false);
     STEP(1, kb + 1, false);
   }
-  if (kb < nkb_int) {
-    STEP(0, kb, false);
-    ++kb;
+  for (; kb < nkb; kb += 2) {
+    STEP(0, kb, true);
+    if (kb + 1 < nkb) STEP(1, kb + 1, true);
   }
-  for (; kb < nkb; ++kb) STEP(kb & 1, kb, true);
 #undef STEP
 
 #undef LOAD_TILE
   // Epilogue: one normalisation per row, bf16 store, log-sum-exp.
-  const float lt = l + xor32(l);
+  const float lt = sum_halves(l);
   const float inv = 1.f / lt;
   if (qi < N) {
     __bf16* orow = O + head_off + (int64_t)qi * rs;

@@ -36,7 +36,6 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 template <int D>
 struct Geo8 {
@@ -59,9 +58,34 @@ __device__ __forceinline__ void copy_to_lds16(__amdgpu_buffer_rsrc_t r, char* ld
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 16, voff, soff, 0, 0);
 }
 
-__device__ __forceinline__ i32x2 read_tr8(const char* lds_generic_base, int byte_off) {
-  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-      (lds_i32x2*)((__attribute__((address_space(3))) char*)lds_generic_base + byte_off));
+// LDS byte address of a generic pointer into LDS.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Transposed LDS read (ds_read_b64_tr_b8) at LDS address addr + OFF, issued
+// as assembly: with the builtin, the compiler's wait-count pass drains vmcnt
+// before it (it cannot tell the read from the in-flight buffer_load ... lds
+// copies of the next tile), while the tile loop's own vmcnt wait and barrier
+// already order them.  The result is valid after lds_wait_v().
+template <int OFF>
+__device__ __forceinline__ i32x2 read_tr8(uint32_t addr) {
+  i32x2 r;
+  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+// Waits for every outstanding LDS read, passing the V^T fragments through so
+// that no use of them is scheduled before the wait.
+template <int NE>
+__device__ __forceinline__ void lds_wait_v(i32x8 (&vf)[2][NE]) {
+  static_assert(NE == 4 || NE == 2, "d = 128 or 64");
+  if constexpr (NE == 4)
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(vf[0][0]), "+v"(vf[0][1]), "+v"(vf[0][2]), "+v"(vf[0][3]),
+                   "+v"(vf[1][0]), "+v"(vf[1][1]), "+v"(vf[1][2]), "+v"(vf[1][3]));
+  else
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(vf[0][0]), "+v"(vf[0][1]), "+v"(vf[1][0]), "+v"(vf[1][1]));
 }
 
 // -inf for keys >= N and, when causal, keys after query qi.  k0: first key.
@@ -151,7 +175,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
       kaddr[t][c] = li * G::RB + (((4 * t + 2 * hh + c) ^ G::swz_k(li)) * 16);
   // V^T operand, transposed read r of k-step u: source lane 2j + q of group g
   // points at key 64u + 16r + 8(j/4) + 4(g/2) + j%4, dims 32e + 16(g%2) + 8q.
-  int vaddr[D / 32];
+  uint32_t vaddr[D / 32];  // LDS addresses in stage 0's V buffer
   {
     const int src = lane & 15, g = lane >> 4;
     const int j = src >> 1, q = src & 1;
@@ -159,7 +183,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
 #pragma unroll
     for (int e = 0; e < D / 32; ++e) {
       const int c = 2 * e + (g & 1);
-      vaddr[e] = kl * G::RB + ((c ^ G::swz_v(kl)) * 16) + 8 * q;
+      vaddr[e] = lds_addr(smem) + G::TILE + kl * G::RB + ((c ^ G::swz_v(kl)) * 16) + 8 * q;
     }
   }
 
@@ -185,7 +209,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     if (CAUSAL && k0 > q0 + 31) continue; /* this and later tiles are after the wave's rows */       \
                                                                                                      \
     const char* kt = smem + stage * G::STAGE;                                                        \
-    const char* vt = kt + G::TILE;                                                                   \
                                                                                                      \
     i32x8 kf[4][D / 64];                                                                             \
 _Pragma("unroll")                                                                                    \
@@ -219,8 +242,7 @@ _Pragma("unroll")                                                               
       mx0 = fmaxf(mx0, fmaxf(sacc[1][v], sacc[1][v + 1]));                                           \
       mx1 = fmaxf(mx1, fmaxf(sacc[3][v], sacc[3][v + 1]));                                           \
     }                                                                                                \
-    float mx = fmaxf(mx0, mx1);                                                                      \
-    mx = fmaxf(mx, xor32(mx));                                                                       \
+    const float mx = max_halves(fmaxf(mx0, mx1));                                                    \
     const float m_new = fmaxf(m, mx * c_tile);                                                       \
     const float alpha = exp2_fast(m - m_new);                                                        \
     m = m_new;                                                                                       \
@@ -249,14 +271,21 @@ _Pragma("unroll")                                                               
                                                                                                      \
     i32x8 vf[2][D / 32];                                                                             \
 _Pragma("unroll")                                                                                    \
-    for (int u = 0; u < 2; ++u)                                                                      \
-_Pragma("unroll")                                                                                    \
-      for (int e = 0; e < D / 32; ++e) {                                                             \
-        i32x2 r[4];                                                                                  \
-_Pragma("unroll")                                                                                    \
-        for (int rr = 0; rr < 4; ++rr) r[rr] = read_tr8(vt, vaddr[e] + (64 * u + 16 * rr) * G::RB);  \
-        vf[u][e] = i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};    \
-      }                                                                                              \
+    for (int e = 0; e < D / 32; ++e) {                                                               \
+      const uint32_t va = vaddr[e] + stage * G::STAGE;                                               \
+      i32x2 r[8];                                                                                    \
+      r[0] = read_tr8<0 * G::RB>(va);                                                                \
+      r[1] = read_tr8<16 * G::RB>(va);                                                               \
+      r[2] = read_tr8<32 * G::RB>(va);                                                               \
+      r[3] = read_tr8<48 * G::RB>(va);                                                               \
+      r[4] = read_tr8<64 * G::RB>(va);                                                               \
+      r[5] = read_tr8<80 * G::RB>(va);                                                               \
+      r[6] = read_tr8<96 * G::RB>(va);                                                               \
+      r[7] = read_tr8<112 * G::RB>(va);                                                              \
+      vf[0][e] = i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};      \
+      vf[1][e] = i32x8{r[4][0], r[4][1], r[5][0], r[5][1], r[6][0], r[6][1], r[7][0], r[7][1]};      \
+    }                                                                                                \
+    lds_wait_v(vf);                                                                                  \
                                                                                                      \
 _Pragma("unroll")                                                                                    \
     for (int u = 0; u < 2; ++u)                                                                      \
@@ -274,7 +303,7 @@ _Pragma("unroll")                                                               
 #undef LOAD_TILE
 #undef TILE_BODY
 
-  const float lt = l + xor32(l);
+  const float lt = sum_halves(l);
   const float inv = sv_prev / lt;
   if (qi < N) {
     __bf16* orow = O + head_off + (int64_t)qi * rs;

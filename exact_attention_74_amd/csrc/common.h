@@ -42,6 +42,28 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// Both half-waves' values of x in every lane: lo = x of lane l % 32, hi = x of
+// lane l % 32 + 32.  One v_permlane32_swap (a VALU lane swap, no LDS round
+// trip) exchanges row 1 of its first operand with row 0 of its second; both
+// start as x.  Written as assembly because the compiler folds the builtin's
+// two results into one when both operands are the same value.  The s_nop
+// covers the VALU-write -> permlane-read hazard.
+__device__ __forceinline__ void halves(float x, float& lo, float& hi) {
+  lo = x;
+  hi = x;
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(lo), "+v"(hi));
+}
+__device__ __forceinline__ float max_halves(float x) {
+  float lo, hi;
+  halves(x, lo, hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  float lo, hi;
+  halves(x, lo, hi);
+  return lo + hi;
+}
+
 // Two fp32 -> packed bf16x2 (round to nearest even).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
