@@ -199,16 +199,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
 
   // Interior tiles (no key past the end, no key after any of the workgroup's
   // query rows) run a copy of the tile body without masking; the few edge
-  // tiles at the end run the masked copy.
-#define TILE_BODY(MASKED)                                                                            \
-    const int k0 = kb * kBC;                                                                         \
-    const int stage = kb & 1;                                                                        \
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                                 \
-    __syncthreads();                                                                                 \
-    if (kb + 1 < nkb) LOAD_TILE(stage ^ 1, k0 + kBC);                                                \
-    if (CAUSAL && k0 > q0 + 31) continue; /* this and later tiles are after the wave's rows */       \
-                                                                                                     \
-    const char* kt = smem + stage * G::STAGE;                                                        \
+  // tiles at the end run the masked copy.  Tile kb sits in LDS stage kb % 2;
+  // both loops take tiles in pairs from an even index, so ST is a
+  // compile-time constant and every LDS offset an immediate.
+#define TILE_BODY(ST, MASKED)                                                                        \
+    const char* kt = smem + (ST) * G::STAGE;                                                         \
                                                                                                      \
     i32x8 kf[4][D / 64];                                                                             \
 _Pragma("unroll")                                                                                    \
@@ -231,23 +226,20 @@ _Pragma("unroll")                                                               
                                                                                                      \
     const float c_tile = scale_log2 * sq * sk_bh[kb];                                                \
     const float sv = sv_bh[kb];                                                                      \
-    float mx0 = fmaxf(sacc[0][0], sacc[0][1]), mx1 = fmaxf(sacc[2][0], sacc[2][1]);                  \
+    /* four chains of three-input maxima (v_max3), one per 32-key block */                          \
+    float mxj[4];                                                                                    \
 _Pragma("unroll")                                                                                    \
-    for (int v = 2; v < 16; v += 2) {                                                                \
-      mx0 = fmaxf(mx0, fmaxf(sacc[0][v], sacc[0][v + 1]));                                           \
-      mx1 = fmaxf(mx1, fmaxf(sacc[2][v], sacc[2][v + 1]));                                           \
-    }                                                                                                \
+    for (int j = 0; j < 4; ++j) {                                                                    \
+      mxj[j] = fmaxf(sacc[j][0], sacc[j][1]);                                                        \
 _Pragma("unroll")                                                                                    \
-    for (int v = 0; v < 16; v += 2) {                                                                \
-      mx0 = fmaxf(mx0, fmaxf(sacc[1][v], sacc[1][v + 1]));                                           \
-      mx1 = fmaxf(mx1, fmaxf(sacc[3][v], sacc[3][v + 1]));                                           \
+      for (int v = 2; v < 16; v += 2) mxj[j] = fmaxf(fmaxf(mxj[j], sacc[j][v]), sacc[j][v + 1]);     \
     }                                                                                                \
-    const float mx = max_halves(fmaxf(mx0, mx1));                                                    \
+    const float mx = max_halves(fmaxf(fmaxf(mxj[0], mxj[1]), fmaxf(mxj[2], mxj[3])));                \
     const float m_new = fmaxf(m, mx * c_tile);                                                       \
     const float alpha = exp2_fast(m - m_new);                                                        \
     m = m_new;                                                                                       \
     const float neg_m = -m;                                                                          \
-    float rsum = 0.f;                                                                                \
+    float rs4[4] = {0.f, 0.f, 0.f, 0.f}; /* four partial sums: short dependency chains */           \
     i32x8 pf[2];                                                                                     \
 _Pragma("unroll")                                                                                    \
     for (int u = 0; u < 2; ++u)                                                                      \
@@ -259,11 +251,11 @@ _Pragma("unroll")                                                               
 _Pragma("unroll")                                                                                    \
         for (int i = 0; i < 4; ++i) {                                                                \
           p[i] = exp2_fast(__builtin_fmaf(sa[r0 + i], c_tile, neg_m));                               \
-          rsum += p[i];                                                                              \
+          rs4[i] += p[i];                                                                            \
         }                                                                                            \
         pf[u][w] = (int)pack_fp8x4(p[0], p[1], p[2], p[3]);                                          \
       }                                                                                              \
-    l = l * alpha + rsum;                                                                            \
+    l = l * alpha + ((rs4[0] + rs4[1]) + (rs4[2] + rs4[3]));                                         \
     const float f = alpha * (sv_prev / sv);                                                          \
     sv_prev = sv;                                                                                    \
 _Pragma("unroll")                                                                                    \
@@ -272,16 +264,16 @@ _Pragma("unroll")                                                               
     i32x8 vf[2][D / 32];                                                                             \
 _Pragma("unroll")                                                                                    \
     for (int e = 0; e < D / 32; ++e) {                                                               \
-      const uint32_t va = vaddr[e] + stage * G::STAGE;                                               \
+      const uint32_t va = vaddr[e];                                                                  \
       i32x2 r[8];                                                                                    \
-      r[0] = read_tr8<0 * G::RB>(va);                                                                \
-      r[1] = read_tr8<16 * G::RB>(va);                                                               \
-      r[2] = read_tr8<32 * G::RB>(va);                                                               \
-      r[3] = read_tr8<48 * G::RB>(va);                                                               \
-      r[4] = read_tr8<64 * G::RB>(va);                                                               \
-      r[5] = read_tr8<80 * G::RB>(va);                                                               \
-      r[6] = read_tr8<96 * G::RB>(va);                                                               \
-      r[7] = read_tr8<112 * G::RB>(va);                                                              \
+      r[0] = read_tr8<(ST) * G::STAGE + 0 * G::RB>(va);                                              \
+      r[1] = read_tr8<(ST) * G::STAGE + 16 * G::RB>(va);                                             \
+      r[2] = read_tr8<(ST) * G::STAGE + 32 * G::RB>(va);                                             \
+      r[3] = read_tr8<(ST) * G::STAGE + 48 * G::RB>(va);                                             \
+      r[4] = read_tr8<(ST) * G::STAGE + 64 * G::RB>(va);                                             \
+      r[5] = read_tr8<(ST) * G::STAGE + 80 * G::RB>(va);                                             \
+      r[6] = read_tr8<(ST) * G::STAGE + 96 * G::RB>(va);                                             \
+      r[7] = read_tr8<(ST) * G::STAGE + 112 * G::RB>(va);                                            \
       vf[0][e] = i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};      \
       vf[1][e] = i32x8{r[4][0], r[4][1], r[5][0], r[5][1], r[6][0], r[6][1], r[7][0], r[7][1]};      \
     }                                                                                                \
@@ -292,14 +284,29 @@ _Pragma("unroll")                                                               
 _Pragma("unroll")                                                                                    \
       for (int e = 0; e < D / 32; ++e) oacc[e] = mfma_fp8(vf[u][e], pf[u], oacc[e]);                 \
 
-  const int nkb_int = min(nkb, min(CAUSAL ? qblk * (kBR / kBC) : nkb, N / kBC));
+#define STEP8(ST, KB, MASKED)                                                                        \
+  do {                                                                                               \
+    const int kb = (KB);                                                                             \
+    const int k0 = kb * kBC;                                                                         \
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                                 \
+    __syncthreads(); /* tile kb resident; every wave is done with the other stage */                 \
+    if (kb + 1 < nkb) LOAD_TILE((ST) ^ 1, k0 + kBC);                                                 \
+    if (!(CAUSAL && k0 > q0 + 31)) { /* else the tile is after all of this wave's rows */            \
+      TILE_BODY(ST, MASKED)                                                                          \
+    }                                                                                                \
+  } while (0)
+  const int nkb_int = min(nkb, min(CAUSAL ? qblk * (kBR / kBC) : nkb, N / kBC)) & ~1;
   LOAD_TILE(0, 0);
-  for (int kb = 0; kb < nkb_int; ++kb) {
-    TILE_BODY(false);
+  int kb2 = 0;
+  for (; kb2 < nkb_int; kb2 += 2) {
+    STEP8(0, kb2, false);
+    STEP8(1, kb2 + 1, false);
   }
-  for (int kb = nkb_int; kb < nkb; ++kb) {
-    TILE_BODY(true);
+  for (; kb2 < nkb; kb2 += 2) {
+    STEP8(0, kb2, true);
+    if (kb2 + 1 < nkb) STEP8(1, kb2 + 1, true);
   }
+#undef STEP8
 #undef LOAD_TILE
 #undef TILE_BODY
 

@@ -74,8 +74,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // Four fp32 -> four e4m3 bytes (round to nearest even), byte i = x_i.
+// The first convert's "old" operand only supplies the upper word, which the
+// second convert overwrites; passing x0's bits (instead of 0) lets it reuse a
+// live register rather than materialise a zero.
 __device__ __forceinline__ uint32_t pack_fp8x4(float x0, float x1, float x2, float x3) {
-  int p = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  int p = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, __builtin_bit_cast(int, x0), false);
   p = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, p, true);
   return (uint32_t)p;
 }
