@@ -36,6 +36,8 @@
 // at most 2^8 and O, l stay consistent with the offset, so O / l and the LSE
 // are unchanged while most blocks skip the O rescale entirely.  The decision
 // is per row, so a row's arithmetic depends on its own visible keys only.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -88,6 +90,33 @@ __device__ __forceinline__ bf16x4 read_tr16(uint32_t addr) {
   return r;
 }
 
+// 16-byte LDS read at addr + OFF, issued as assembly so that the reads of a
+// tile can run several MFMAs ahead; waited for with wait_lds<N>().
+template <int OFF>
+__device__ __forceinline__ bf16x8 read_b128(uint32_t addr) {
+  bf16x8 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+// Waits until at most N of this wave's LDS reads are outstanding, passing x
+// through so that no use of x is scheduled before the wait.
+template <int N>
+__device__ __forceinline__ void wait_lds(bf16x8& x) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "n"(N));
+}
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(IC<I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // Waits for every outstanding LDS read, passing the V^T fragments through so
 // that no use of them is scheduled before the wait.
 template <int NE>
@@ -134,25 +163,31 @@ __device__ __forceinline__ float rowmax(const f32x16 (&s)[2]) {
 // lazy offset, and O^T += V^T P^T.  smem: the LDS tile buffers; vaddr: LDS
 // addresses of this lane's V^T fragment sources in stage 0's V buffer.
 template <int D, bool CAUSAL, bool MASKED, int ST>
-__device__ __forceinline__ void tile_compute(const char* smem, const int (&kaddr)[D / 16],
+__device__ __forceinline__ void tile_compute(const char* smem, const uint32_t (&kaddr)[D / 16],
                                              const uint32_t (&vaddr)[D / 32],
                                              const bf16x8 (&qf)[D / 16], f32x16 (&oacc)[D / 32],
                                              float& m, float& l, int k0, int N, int qi, int hh,
                                              float scale_log2) {
   using G = Geo<D>;
-  const char* kt = smem + ST * G::STAGE;
-  // S^T = K Q^T: two 32-key blocks.  All K fragments are read first.
-  bf16x8 kf[2][D / 16];
-#pragma unroll
-  for (int t = 0; t < D / 16; ++t)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) kf[j][t] = *(const bf16x8*)(kt + kaddr[t] + j * 32 * G::RB);
+  // S^T = K Q^T: two 32-key blocks.  Fragment i = 2t + j (k-step t, block
+  // j); the reads run AHEAD fragments ahead of the MFMAs (the loop's barrier
+  // has drained this wave's LDS reads, so lgkmcnt counts only these).
+  constexpr int NK = 2 * (D / 16);
+  constexpr int AHEAD = 8;
+  bf16x8 kf[NK];
+  auto rd = [&](auto I) __attribute__((always_inline)) {
+    constexpr int i = decltype(I)::value, t = i / 2, j = i % 2;
+    kf[i] = read_b128<ST * G::STAGE + j * 32 * G::RB>(kaddr[t]);
+  };
+  static_for<AHEAD>(rd);
   f32x16 sacc[2];
-  sacc[0] = sacc[1] = f32x16{};
-#pragma unroll
-  for (int t = 0; t < D / 16; ++t)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) sacc[j] = mfma_bf16(kf[j][t], qf[t], sacc[j]);
+  static_for<NK>([&](auto I) __attribute__((always_inline)) {
+    constexpr int i = decltype(I)::value, t = i / 2, j = i % 2;
+    constexpr int issued = (AHEAD + i < NK) ? AHEAD + i : NK;
+    wait_lds<issued - i - 1>(kf[i]);
+    sacc[j] = mfma_bf16(kf[i], qf[t], t == 0 ? f32x16{} : sacc[j]);
+    if constexpr (i + AHEAD < NK) rd(IC<i + AHEAD>{});
+  });
   // V^T fragments for this tile's P.V, read before the softmax so that the
   // exp/sum work covers their latency.
   bf16x8 vf[4][D / 32];
@@ -266,9 +301,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
   } while (0)
 
   // LDS byte offsets (within a tile) of this lane's operand fragments.
-  int kaddr[D / 16];  // K rows li (+32 for the second block), chunk 2t + hh
+  uint32_t kaddr[D / 16];  // LDS addresses: K rows li (+32 for the second block), chunk 2t + hh
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) kaddr[t] = li * G::RB + (((2 * t + hh) ^ G::swz_k(li)) * 16);
+  for (int t = 0; t < D / 16; ++t)
+    kaddr[t] = lds_addr(smem) + li * G::RB + (((2 * t + hh) ^ G::swz_k(li)) * 16);
   uint32_t vaddr[D / 32];  // transposed-read source: key 4h + j, dims 32e + 16(g%2) + 4q
   {
     const int src = lane & 15, g = lane >> 4;
