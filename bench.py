@@ -1,13 +1,16 @@
 #!/usr/bin/env python3
 """Benchmark of the attention forward hot path on one MI355X.
 
-One step = the whole path over one batch of synthetic input (B=4, H=16,
-N=8192, d=128, non-causal, inputs resident in HBM):
-  blockquant_hadamard(Q), (K) with the seeded sign vector, (V) without,
-  attn_fwd_fp8 on the codes, and attn_fwd_bf16 on bf16 N(0,1) inputs.
+One step = the whole path over one batch of synthetic input (d=128, N=8192,
+non-causal, inputs resident in HBM):
+  fp8 leg, B=4 H=16 (N(0,1) with 0.1% of entries x30, seed 3):
+    blockquant_hadamard(Q), (K) with the seeded sign vector, (V) without,
+    then attn_fwd_fp8 on the codes;
+  bf16 leg, B=2 H=16 (the N=8192 point of the 16384-token sweep, N(0,1),
+    seed 2): attn_fwd_bf16.
 Each launch is bracketed by HIP events on the stream it runs on; the printed
-``value`` is the bf16 attention TFLOP/s (4*B*H*N^2*d per launch over its mean
-event time), with the fp8 figure and the pre-pass GB/s beside it.
+``value`` is the bf16 attention TFLOP/s (4*B*H*N^2*d per launch over its
+median event time), with the fp8 figure and the pre-pass GB/s beside it.
 
 Prints ONE JSON line (see the repository's design notes for every field).
 """
@@ -32,14 +35,15 @@ CALIB_COPY_BYTES = 256 << 20
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--causal", action="store_true", help="time the causal variant instead")
     p.add_argument("--N", type=int, default=8192)
-    p.add_argument("--B", type=int, default=4)
+    p.add_argument("--B", type=int, default=2, help="batch of the bf16 leg")
+    p.add_argument("--B8", type=int, default=4, help="batch of the fp8 leg")
     p.add_argument("--H", type=int, default=16)
     p.add_argument("--d", type=int, default=128)
     p.add_argument("--calib-copy", action="store_true",
@@ -120,10 +124,11 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w16 = workloads.Workload(f"attn_fwd_b{a.B}h{a.H}n{a.N}d{a.d}" + ("_causal" if a.causal else ""),
-                             a.B, a.H, a.N, a.d, a.causal, seed=3)
-    w8 = workloads.Workload(w16.name + "_fp8_outlier30", a.B, a.H, a.N, a.d, a.causal, seed=3,
-                            dist="outlier30")
+    sfx = "_causal" if a.causal else ""
+    w16 = workloads.Workload(f"attn_fwd_b{a.B}h{a.H}n{a.N}d{a.d}{sfx}", a.B, a.H, a.N, a.d,
+                             a.causal, seed=2)
+    w8 = workloads.Workload(f"attn_fwd_b{a.B8}h{a.H}n{a.N}d{a.d}{sfx}_fp8_outlier30", a.B8, a.H,
+                            a.N, a.d, a.causal, seed=3, dist="outlier30")
 
     def dev_bf16(x):
         return torch.from_numpy(x).to(torch.bfloat16).to(dev)
@@ -131,14 +136,14 @@ def main():
     q, k, v = (dev_bf16(x) for x in workloads.gen_qkv(w16))
     q8in, k8in, v8in = (dev_bf16(x) for x in workloads.gen_qkv(w8))
     signs = torch.from_numpy(workloads.gen_signs(a.d)).to(dev)
-    B, H, N, d = a.B, a.H, a.N, a.d
+    B, B8, H, N, d = a.B, a.B8, a.H, a.N, a.d
     nsb = (N + 127) // 128
     o16 = torch.empty_like(q)
     lse16 = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    o8 = torch.empty_like(q)
-    lse8 = torch.empty_like(lse16)
-    codes = [torch.empty((B, N, H, d), dtype=torch.uint8, device=dev) for _ in range(3)]
-    scales = [torch.empty((B, H, nsb), dtype=torch.float32, device=dev) for _ in range(3)]
+    o8 = torch.empty_like(q8in)
+    lse8 = torch.empty((B8, H, N), dtype=torch.float32, device=dev)
+    codes = [torch.empty((B8, N, H, d), dtype=torch.uint8, device=dev) for _ in range(3)]
+    scales = [torch.empty((B8, H, nsb), dtype=torch.float32, device=dev) for _ in range(3)]
     scale = w16.softmax_scale
     stream = torch.cuda.current_stream(dev)
 
@@ -187,14 +192,15 @@ def main():
     mean = {n: float(np.mean(v)) for n, v in per.items()}
     med = {n: float(np.median(v)) for n, v in per.items()}
 
-    flops = w16.flops()
-    t16 = mean["attn_fwd_bf16"] * 1e-3
-    t8 = mean["attn_fwd_fp8"] * 1e-3
-    tf16 = flops / t16 / 1e12
-    tf8 = flops / t8 / 1e12
+    t16 = med["attn_fwd_bf16"] * 1e-3
+    t8 = med["attn_fwd_fp8"] * 1e-3
+    tf16 = w16.flops() / t16 / 1e12
+    tf8 = w8.flops() / t8 / 1e12
+    tf16_best = w16.flops() / (min(per["attn_fwd_bf16"]) * 1e-3) / 1e12
+    tf8_best = w8.flops() / (min(per["attn_fwd_fp8"]) * 1e-3) / 1e12
     # pre-pass algorithmic bytes per tensor: read bf16, write e4m3, write fp32 scales
-    bq_bytes = B * N * H * d * (2 + 1) + B * H * nsb * 4
-    t_bq = np.mean([mean["blockquant_q"], mean["blockquant_k"], mean["blockquant_v"]]) * 1e-3
+    bq_bytes = B8 * N * H * d * (2 + 1) + B8 * H * nsb * 4
+    t_bq = np.median([med["blockquant_q"], med["blockquant_k"], med["blockquant_v"]]) * 1e-3
     ok = bool(torch.isfinite(o16).all().item() and torch.isfinite(o8).all().item())
 
     out = {
@@ -213,10 +219,12 @@ def main():
         "config": {"workload": w16.name, "B": B, "H": H, "N": N, "d": d, "causal": a.causal,
                    "softmax_scale": scale, "global_batch": B, "seq_len": N,
                    "parallelism": "single GPU (heads and query blocks across CUs)"},
+        "timing": "median of the per-launch HIP event times over the timed steps",
         "pct_of_peak": round(100 * tf16 / PEAK_BF16_TFLOPS, 2),
+        "best": {"attn_fwd_bf16": round(tf16_best, 2), "attn_fwd_fp8": round(tf8_best, 2)},
         "fp8": {"value": round(tf8, 2), "unit": "TFLOP/s", "dtype": "fp8 e4m3",
                 "pct_of_peak": round(100 * tf8 / PEAK_FP8_TFLOPS, 2),
-                "workload": w8.name, "ms": round(mean["attn_fwd_fp8"], 4)},
+                "workload": w8.name, "B": B8, "ms": round(med["attn_fwd_fp8"], 4)},
         "blockquant_hadamard": {"gbps": round(bq_bytes / t_bq / 1e9, 1),
                                 "pct_of_hbm_peak": round(100 * bq_bytes / t_bq / 1e9 / PEAK_HBM_GBS, 2),
                                 "bytes_per_launch": bq_bytes, "us": round(t_bq * 1e6, 2)},
@@ -227,7 +235,7 @@ def main():
                      "frac": round(tf16 / PEAK_BF16_TFLOPS, 4),
                      "traffic": profiled_traffic("attn_fwd_bf16", f"attn_fwd_b{B}h{H}n{N}d{d}"
                                                  if not a.causal else "none"),
-                     "algorithmic_flops_per_launch": flops},
+                     "algorithmic_flops_per_launch": w16.flops()},
         "outputs_finite": ok,
     }
     if not a.no_cpu_baseline:

@@ -19,7 +19,7 @@ namespace exattn {
 namespace {
 
 constexpr int kRows = 128;
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 
 enum Mode { kQuantBlock = 0, kAmaxOnly = 1, kQuantGiven = 2 };
 
@@ -96,21 +96,18 @@ __global__ __launch_bounds__(kThreads) void blockquant_kernel(const __bf16* __re
               y[p][c][k] = a + b2;
               y[p][c][k + st] = a - b2;
             }
-      // strides 8, 16: across the row's 4 lanes
+      // strides 8, 16: across the row's 4 lanes.  The lower lane of a pair
+      // keeps y + partner, the upper one partner - y: partner + sgn * y with
+      // sgn = -1 on the upper lane (one fma, exact sign, one rounding).
+      const float sg8 = (lr & 1) ? -1.f : 1.f, sg16 = (lr & 2) ? -1.f : 1.f;
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float o = quad_xor<1>(y[p][c][k]);
-          y[p][c][k] = (lr & 1) ? (o - y[p][c][k]) : (y[p][c][k] + o);
-        }
+        for (int k = 0; k < 8; ++k) y[p][c][k] = __builtin_fmaf(sg8, y[p][c][k], quad_xor<1>(y[p][c][k]));
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float o = quad_xor<2>(y[p][c][k]);
-          y[p][c][k] = (lr & 2) ? (o - y[p][c][k]) : (y[p][c][k] + o);
-        }
+        for (int k = 0; k < 8; ++k) y[p][c][k] = __builtin_fmaf(sg16, y[p][c][k], quad_xor<2>(y[p][c][k]));
       // strides 32, 64: across this lane's chunks
 #pragma unroll
       for (int st = 1; st < NC; st <<= 1)
