@@ -1,8 +1,11 @@
 // bf16 exact-attention forward for gfx950.
 //
 // Work decomposition (FA2 query-block parallelism, "Efficient Attention &
-// FlashAttention" M4-054): one workgroup of 8 waves per (b, h, block of 256
-// query rows); each wave owns 32 query rows, two waves share a SIMD.  The
+// FlashAttention" M4-054): one workgroup per (b, h, block of query rows);
+// each wave owns 32 query rows and two waves share a SIMD.  Long sequences use
+// 8-wave workgroups (256 rows; one per CU, so a K/V tile in LDS serves 256
+// rows), short ones 4-wave workgroups (128 rows; two per CU, so one
+// workgroup's start-up and epilogue overlap the other's key tiles).  The
 // key/value sequence is streamed in blocks of 64 keys with the online-softmax
 // recurrence of the FlashAttention-3 report, section 3 (running max m,
 // running sum l, one final normalisation).
@@ -26,9 +29,9 @@
 // and the ds_read_b64_tr_b16 transposed reads of the V operand are free of
 // bank conflicts; the V tile stays key-major in LDS and the transposed read
 // produces V^T fragments directly.  Reads past the end of the sequence come
-// back as zeros from the buffer descriptor's range check.  Within a tile, all
-// K fragments are read before the S MFMAs, and all V^T fragments before the
-// softmax, whose VALU work then covers their LDS latency.
+// back as zeros from the buffer descriptor's range check.  Within a tile, the
+// K fragment reads run eight MFMAs ahead of the S MFMAs, and all V^T fragments
+// are read before the softmax, whose VALU work then covers their LDS latency.
 //
 // Rescaling (exact, fewer non-matmul FLOPs: "Efficient Attention &
 // FlashAttention", FA2 section).  A row's exp2 offset is raised to its block
@@ -44,10 +47,7 @@
 namespace exattn {
 namespace {
 
-constexpr int kBR = 256;     // query rows per workgroup
 constexpr int kBC = 64;      // keys per KV block
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
 constexpr float kLazy = 8.f;  // rescale threshold (log2 units)
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -59,7 +59,6 @@ struct Geo {
   static constexpr int RP = 256 / RB;        // rows per 256-byte bank cycle
   static constexpr int TILE = kBC * RB;      // bytes per K or V tile
   static constexpr int STAGE = 2 * TILE;     // K + V
-  static constexpr int LOADS = TILE / (1024 * kWaves);  // 1 KB loads per wave per tile
   // chunk position of chunk c of row `row`
   __device__ static int swz_k(int row) { return (row / RP) % CPR; }
   __device__ static int swz_v(int row) { return 4 * ((row / RP) % (CPR / 4)); }
@@ -237,8 +236,11 @@ __device__ __forceinline__ void tile_compute(const char* smem, const uint32_t (&
     for (int e = 0; e < D / 32; ++e) oacc[e] = mfma_bf16(vf[t2][e], pb[t2], oacc[e]);
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
+// NW waves per workgroup (32 query rows each): 8 for long sequences (one
+// workgroup per CU, K/V tiles shared by 256 rows), 4 for short ones (two
+// workgroups per CU, so one's start-up and epilogue overlap the other's tiles).
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int H, int N, float scale_log2, int nqb,
     int xcd_remap) {
@@ -261,6 +263,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
   const int64_t rs = (int64_t)H * D;
   const int64_t head_off = ((int64_t)b * N * H + h) * D;
 
+  constexpr int kBR = 32 * NW;                       // query rows per workgroup
+  constexpr int LOADS = G::TILE / (1024 * NW);        // 1 KB copies per wave per tile
   const int q0 = qblk * kBR + wave * 32;
   const int qi = q0 + li;
 
@@ -282,10 +286,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
   const uint32_t row_bytes = (uint32_t)(rs * 2);
 
   // Per-lane global byte offsets of the chunks this lane deposits into LDS.
-  uint32_t voff_k[G::LOADS], voff_v[G::LOADS];
+  uint32_t voff_k[LOADS], voff_v[LOADS];
 #pragma unroll
-  for (int i = 0; i < G::LOADS; ++i) {
-    const int chunk = (wave * G::LOADS + i) * 64 + lane;  // LDS chunk slot within a tile
+  for (int i = 0; i < LOADS; ++i) {
+    const int chunk = (wave * LOADS + i) * 64 + lane;  // LDS chunk slot within a tile
     const int row = chunk / G::CPR, pos = chunk % G::CPR;
     voff_k[i] = row * row_bytes + (uint32_t)((pos ^ G::swz_k(row)) * 16);
     voff_v[i] = row * row_bytes + (uint32_t)((pos ^ G::swz_v(row)) * 16);
@@ -293,8 +297,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
 #define LOAD_TILE(stage, k0)                                                                    \
   do {                                                                                          \
     const uint32_t soff_ = (uint32_t)(k0) * row_bytes;                                          \
-    _Pragma("unroll") for (int i_ = 0; i_ < G::LOADS; ++i_) {                                   \
-      char* dst_ = smem + (stage) * G::STAGE + (wave * G::LOADS + i_) * 1024;                   \
+    _Pragma("unroll") for (int i_ = 0; i_ < LOADS; ++i_) {                                   \
+      char* dst_ = smem + (stage) * G::STAGE + (wave * LOADS + i_) * 1024;                   \
       copy_to_lds16(rk, dst_, voff_k[i_], soff_);                                               \
       copy_to_lds16(rv, dst_ + G::TILE, voff_v[i_], soff_);                                     \
     }                                                                                           \
@@ -372,16 +376,29 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
   }
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                  int N, float scale, hipStream_t stream) {
+template <int D, bool CAUSAL, int NW>
+hipError_t launch_nw(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                     int N, float scale, hipStream_t stream) {
+  constexpr int kBR = 32 * NW;
   const int nqb = (N + kBR - 1) / kBR;
   const int64_t grid = (int64_t)B * H * nqb;
   const int remap = (grid % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, NW>), dim3((unsigned)grid), dim3(64 * NW), 0,
                      stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse,
                      H, N, scale * kLog2e, nqb, remap);
   return hipGetLastError();
+}
+
+// Four-wave workgroups win where a workgroup has few key tiles (short
+// sequences) or the causal work is uneven; crossover measured on the 16384-
+// token sweep (B = 16384 / N): N <= 1024 (d=128) / 2048 (d=64) non-causal,
+// N <= 4096 / 8192 causal.
+template <int D, bool CAUSAL>
+hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                  int N, float scale, hipStream_t stream) {
+  const int small_n = (CAUSAL ? 4096 : 1024) * (128 / D);
+  if (N <= small_n) return launch_nw<D, CAUSAL, 4>(q, k, v, o, lse, B, H, N, scale, stream);
+  return launch_nw<D, CAUSAL, 8>(q, k, v, o, lse, B, H, N, scale, stream);
 }
 
 }  // namespace

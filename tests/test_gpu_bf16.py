@@ -81,6 +81,30 @@ def test_ragged_full_parity(causal, d, N):
     _check(o, lse, o_ref, lse_ref, w.name, absv)
 
 
+@pytest.mark.parametrize("N,d,causal", [(1025, 128, False), (1500, 128, False), (2100, 64, False),
+                                         (4097, 128, True), (8300, 64, True)])
+def test_ragged_eight_wave_path(N, d, causal):
+    """Lengths just past the short-sequence crossover take the 8-wave
+    workgroups (256 query rows); ragged tails of 1 to 63 keys."""
+    w = workloads.Workload(f"ragged8_n{N}_d{d}", 1, 3, N, d, causal, seed=31 + N)
+    say(w.name + ("_causal" if causal else ""))
+    host, dev = bf16_inputs(w)
+    o, lse = _run(dev, causal, w.softmax_scale)
+    if N <= 2100:
+        o_ref, lse_ref = oracle.naive_attention(*host, w.softmax_scale, causal)
+        absv, _ = oracle.naive_attention(host[0], host[1], np.abs(host[2]), w.softmax_scale, causal)
+        _check(o, lse, o_ref, lse_ref, w.name, absv)
+    else:
+        rows = workloads.sample_rows(w.B, w.H, w.N, 512, seed=N)
+        # the last rows of every head (the ragged q-block) are always checked
+        tail = np.array([(0, h, n) for h in range(w.H) for n in range(N - 5, N)])
+        rows = np.concatenate([rows, tail])
+        o_ref, l_ref = oracle.naive_attention_rows(*host, w.softmax_scale, causal, rows)
+        absv, _ = oracle.naive_attention_rows(host[0], host[1], np.abs(host[2]), w.softmax_scale,
+                                              causal, rows)
+        _check(rows_of(o, rows), lse_rows(lse, rows), o_ref, l_ref, w.name, absv)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_d96_zero_padded(causal):
     """d=96 zero-padded to 128 with scale 1/sqrt(96) equals d=96 attention."""
