@@ -14,7 +14,12 @@ Q, K, V the (N x d) slices of the BSHD tensors,
     LSE_i = m_i + ln sum_j exp(S[i, j] - m_i)
 
 The log-sum-exp is the softmax statistic kept for the backward pass ([FA3-blog]
-section 5.4).  A key j is visible to query i iff j <= i (queries and keys have
+section 5.4).
+
+Grouped-query and multi-query attention ([FA3-report] section 3.4, which keeps
+FA-2's index mapping for MQA/GQA): K and V may have H_kv heads with H a
+multiple of H_kv; query head h then uses K/V head h // (H // H_kv) in the
+definition above.  H_kv = H is ordinary multi-head attention.  A key j is visible to query i iff j <= i (queries and keys have
 the same length in every workload here, so top-left and bottom-right causal
 alignment coincide).
 """
@@ -29,6 +34,13 @@ def _heads(x: np.ndarray) -> np.ndarray:
     if x.ndim != 4:
         raise ValueError("expected a BSHD array")
     return np.ascontiguousarray(np.transpose(x, (0, 2, 1, 3)), dtype=np.float64)
+
+
+def kv_head(h: int, H: int, H_kv: int) -> int:
+    """The K/V head that query head h reads when K/V have H_kv heads."""
+    if H_kv < 1 or H % H_kv:
+        raise ValueError(f"H = {H} must be a positive multiple of H_kv = {H_kv}")
+    return h // (H // H_kv)
 
 
 def _rows_softmax_av(s: np.ndarray, vh: np.ndarray):
@@ -49,19 +61,20 @@ def naive_attention(q, k, v, scale: float, causal: bool, row_chunk: int = 512):
     """
     qh, kh, vh = _heads(q), _heads(k), _heads(v)
     B, H, N, d = qh.shape
-    Nk = kh.shape[2]
+    Nk, Hkv = kh.shape[2], kh.shape[1]
     o = np.empty((B, H, N, vh.shape[3]), dtype=np.float64)
     lse = np.empty((B, H, N), dtype=np.float64)
     cols = np.arange(Nk)
     for b in range(B):
         for h in range(H):
+            g = kv_head(h, H, Hkv)
             for r0 in range(0, N, row_chunk):
                 r1 = min(N, r0 + row_chunk)
-                s = scale * (qh[b, h, r0:r1] @ kh[b, h].T)
+                s = scale * (qh[b, h, r0:r1] @ kh[b, g].T)
                 if causal:
                     rows = np.arange(r0, r1)
                     s[cols[None, :] > rows[:, None]] = -np.inf
-                o[b, h, r0:r1], lse[b, h, r0:r1] = _rows_softmax_av(s, vh[b, h])
+                o[b, h, r0:r1], lse[b, h, r0:r1] = _rows_softmax_av(s, vh[b, g])
     return np.transpose(o, (0, 2, 1, 3)), lse
 
 
@@ -83,8 +96,9 @@ def naive_attention_rows(q, k, v, scale: float, causal: bool, rows):
     for key in np.unique(keys):
         sel = np.nonzero(keys == key)[0]
         b, h = int(rows[sel[0], 0]), int(rows[sel[0], 1])
-        kh = np.asarray(k[b, :, h, :], dtype=np.float64)
-        vh = np.asarray(v[b, :, h, :], dtype=np.float64)
+        g = kv_head(h, q.shape[2], k.shape[2])
+        kh = np.asarray(k[b, :, g, :], dtype=np.float64)
+        vh = np.asarray(v[b, :, g, :], dtype=np.float64)
         qi = np.asarray(q[b, rows[sel, 2], h, :], dtype=np.float64)
         s = scale * (qi @ kh.T)
         if causal:
@@ -111,11 +125,12 @@ def tiled_attention(q, k, v, scale: float, causal: bool, Br: int = 64, Bc: int =
     """
     qh, kh, vh = _heads(q), _heads(k), _heads(v)
     B, H, N, d = qh.shape
-    Nk = kh.shape[2]
+    Nk, Hkv = kh.shape[2], kh.shape[1]
     o = np.empty((B, H, N, vh.shape[3]), dtype=np.float64)
     lse = np.empty((B, H, N), dtype=np.float64)
     for b in range(B):
         for h in range(H):
+            g = kv_head(h, H, Hkv)
             for r0 in range(0, N, Br):
                 r1 = min(N, r0 + Br)
                 qi = qh[b, h, r0:r1]
@@ -127,14 +142,14 @@ def tiled_attention(q, k, v, scale: float, causal: bool, Br: int = 64, Bc: int =
                     if causal and c0 > r1 - 1:
                         break
                     c1 = min(Nk, c0 + Bc)
-                    s = scale * (qi @ kh[b, h, c0:c1].T)
+                    s = scale * (qi @ kh[b, g, c0:c1].T)
                     if causal:
                         s[np.arange(c0, c1)[None, :] > rows[:, None]] = -np.inf
                     m_new = np.maximum(m, np.max(s, axis=1))
                     p = np.exp(s - m_new[:, None])
                     alpha = np.exp(m - m_new)
                     l = alpha * l + np.sum(p, axis=1)
-                    acc = alpha[:, None] * acc + p @ vh[b, h, c0:c1]
+                    acc = alpha[:, None] * acc + p @ vh[b, g, c0:c1]
                     m = m_new
                 o[b, h, r0:r1] = acc / l[:, None]
                 lse[b, h, r0:r1] = m + np.log(l)

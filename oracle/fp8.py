@@ -32,6 +32,8 @@ import math
 
 import numpy as np
 
+from .attention import kv_head
+
 E4M3_MAX = 448.0
 QBLOCK = 128  # rows per quantisation block (Br = Bc = 128, [FA3-blog] section 3.1)
 
@@ -193,7 +195,9 @@ def fp8_attention_emulation(q8, k8, v8, sq, sk, sv, scale: float, causal: bool,
                             Bc: int = QBLOCK, quantize_p: bool = True, rows=None):
     """FP8 attention forward as the FP8 path computes it, in fp64.
 
-    Inputs are e4m3 codes (BSHD) and per-128-row block scales [B,H,ceil(N/128)].
+    Inputs are e4m3 codes (BSHD) and per-128-row block scales [B,H,ceil(N/128)];
+    K/V codes and scales may have H_kv heads (query head h then reads K/V head
+    h // (H // H_kv), as in ``oracle.attention.kv_head``).
     The online-softmax recurrence of ``oracle.attention.tiled_attention`` runs
     over key blocks of Bc, with:
       S_j = (Q8 K8_j^T) * sQ * sK_j * scale  (block scaling of S, [FA3-report] 3.3)
@@ -205,12 +209,13 @@ def fp8_attention_emulation(q8, k8, v8, sq, sk, sv, scale: float, causal: bool,
     """
     qv, kv, vv = e4m3_decode(q8), e4m3_decode(k8), e4m3_decode(v8)
     B, N, H, d = qv.shape
-    Nk = kv.shape[1]
+    Nk, Hkv = kv.shape[1], kv.shape[2]
     sq = np.asarray(sq, np.float64)
     sk = np.asarray(sk, np.float64)
     sv = np.asarray(sv, np.float64)
 
     def one(b, h, qi_idx):
+        g = kv_head(h, H, Hkv)
         qi = qv[b, qi_idx, h, :]
         sqr = sq[b, h, qi_idx // QBLOCK]
         m = np.full(len(qi_idx), -np.inf)
@@ -221,9 +226,9 @@ def fp8_attention_emulation(q8, k8, v8, sq, sk, sv, scale: float, causal: bool,
             if causal and c0 > qi_idx.max():
                 break
             keys = np.arange(c0, c1)
-            skc = sk[b, h, keys // QBLOCK]
-            svc = sv[b, h, keys // QBLOCK]
-            s = (qi @ kv[b, c0:c1, h, :].T) * (sqr[:, None] * skc[None, :]) * scale
+            skc = sk[b, g, keys // QBLOCK]
+            svc = sv[b, g, keys // QBLOCK]
+            s = (qi @ kv[b, c0:c1, g, :].T) * (sqr[:, None] * skc[None, :]) * scale
             if causal:
                 s[keys[None, :] > qi_idx[:, None]] = -np.inf
             m_new = np.maximum(m, np.max(s, axis=1))
@@ -231,7 +236,7 @@ def fp8_attention_emulation(q8, k8, v8, sq, sk, sv, scale: float, causal: bool,
             alpha = np.exp(m - m_new)
             l = alpha * l + np.sum(p, axis=1)
             pq = e4m3_decode(e4m3_encode(p)) if quantize_p else p
-            acc = alpha[:, None] * acc + pq @ (vv[b, c0:c1, h, :] * svc[:, None])
+            acc = alpha[:, None] * acc + pq @ (vv[b, c0:c1, g, :] * svc[:, None])
             m = m_new
         return acc / l[:, None], m + np.log(l)
 

@@ -142,3 +142,76 @@ def test_causal_prefix_independence():
     assert np.allclose(o2[:, :40], o1[:, :40], rtol=1e-13, atol=1e-14)
     assert np.allclose(l2[:, :, :40], l1[:, :, :40], rtol=1e-13, atol=1e-14)
     assert not np.allclose(o2[:, 40:], o1[:, 40:])
+
+
+# --- grouped-query / multi-query attention ([FA3-report] section 3.4) -------
+
+def _sdpa_gqa(q, k, v, scale, causal):
+    """torch CPU fp64 SDPA with its own grouped-query head mapping (enable_gqa)."""
+    qt = torch.from_numpy(np.transpose(q, (0, 2, 1, 3)).copy())
+    kt = torch.from_numpy(np.transpose(k, (0, 2, 1, 3)).copy())
+    vt = torch.from_numpy(np.transpose(v, (0, 2, 1, 3)).copy())
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=causal, scale=scale,
+                                                         enable_gqa=True)
+    return np.transpose(o.numpy(), (0, 2, 1, 3))
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 2), (6, 3), (4, 1), (3, 3)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_matches_torch_sdpa(H, Hkv, causal):
+    q = _rand((2, 70, H, 16), 40)
+    k = _rand((2, 70, Hkv, 16), 41)
+    v = _rand((2, 70, Hkv, 16), 42)
+    o, _ = naive_attention(q, k, v, 0.3, causal)
+    np.testing.assert_allclose(o, _sdpa_gqa(q, k, v, 0.3, causal), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 2), (4, 1)])
+def test_gqa_is_mha_on_replicated_heads(H, Hkv):
+    """Each group of H // Hkv query heads sees the same K/V head: the result is
+    multi-head attention on K/V with every head written out H // Hkv times."""
+    q = _rand((1, 90, H, 32), 43)
+    k = _rand((1, 90, Hkv, 32), 44)
+    v = _rand((1, 90, Hkv, 32), 45)
+    kr = np.concatenate([k[:, :, [g], :] for g in range(Hkv) for _ in range(H // Hkv)], axis=2)
+    vr = np.concatenate([v[:, :, [g], :] for g in range(Hkv) for _ in range(H // Hkv)], axis=2)
+    for causal in (False, True):
+        o, lse = naive_attention(q, k, v, 0.2, causal)
+        o_r, lse_r = naive_attention(q, kr, vr, 0.2, causal)
+        np.testing.assert_array_equal(o, o_r)
+        np.testing.assert_array_equal(lse, lse_r)
+        ot, lset = tiled_attention(q, k, v, 0.2, causal, Br=32, Bc=48)
+        np.testing.assert_allclose(ot, o, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lset, lse, rtol=1e-12, atol=1e-13)
+
+
+def test_mqa_heads_share_one_kv():
+    """H_kv = 1: query head h alone against the single K/V head gives head h."""
+    q = _rand((1, 50, 3, 16), 46)
+    k = _rand((1, 50, 1, 16), 47)
+    v = _rand((1, 50, 1, 16), 48)
+    o, lse = naive_attention(q, k, v, 0.25, True)
+    for h in range(3):
+        oh, lh = naive_attention(q[:, :, [h], :], k, v, 0.25, True)
+        np.testing.assert_array_equal(o[:, :, [h], :], oh)
+        np.testing.assert_array_equal(lse[:, [h], :], lh)
+
+
+def test_gqa_rows_variant_equals_full():
+    q = _rand((2, 64, 6, 16), 49)
+    k = _rand((2, 64, 2, 16), 50)
+    v = _rand((2, 64, 2, 16), 51)
+    o, lse = naive_attention(q, k, v, 0.5, True)
+    rows = np.array([[0, 0, 0], [1, 5, 63], [0, 3, 17], [1, 2, 40]])
+    oo, ll = naive_attention_rows(q, k, v, 0.5, True, rows)
+    for r, (b, h, i) in enumerate(rows):
+        np.testing.assert_allclose(oo[r], o[b, i, h], rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(ll[r], lse[b, h, i], rtol=1e-13, atol=1e-14)
+
+
+def test_kv_head_rejects_bad_counts():
+    from oracle import kv_head
+    assert [kv_head(h, 8, 2) for h in range(8)] == [0, 0, 0, 0, 1, 1, 1, 1]
+    for H, Hkv in ((4, 3), (2, 4), (4, 0)):
+        with pytest.raises(ValueError):
+            kv_head(0, H, Hkv)

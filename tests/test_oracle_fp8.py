@@ -274,3 +274,29 @@ def test_fp8_scheme_reproduces_page_rmse():
     assert abs(fa3 / g["fa3_fp8_block_quant_plus_hadamard_rmse"] - 1.0) < 0.25, fa3
     assert base > 1.5 * fa3, (base, fa3)
     assert base < 1.5 * g["fp8_per_tensor_baseline_rmse"]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_emulation_gqa_is_mha_on_replicated_heads(causal):
+    """K/V codes and scales on H_kv heads give exactly the result of the same
+    codes and scales written out once per query head of the group
+    ([FA3-report] section 3.4, GQA by index mapping)."""
+    H, Hkv, N, d = 6, 2, 200, 64
+    q = workloads.gen_random((1, N, H, d), 70)
+    k = workloads.gen_random((1, N, Hkv, d), 71)
+    v = workloads.gen_random((1, N, Hkv, d), 72)
+    q8, sq = blockquant_hadamard(q)
+    k8, sk = blockquant_hadamard(k)
+    v8, sv = blockquant_hadamard(v)
+    r = H // Hkv
+    heads = [g for g in range(Hkv) for _ in range(r)]
+    o, l = fp8_attention_emulation(q8, k8, v8, sq, sk, sv, 0.125, causal)
+    o_r, l_r = fp8_attention_emulation(q8, k8[:, :, heads], v8[:, :, heads], sq, sk[:, heads],
+                                       sv[:, heads], 0.125, causal)
+    np.testing.assert_array_equal(o, o_r)
+    np.testing.assert_array_equal(l, l_r)
+    rows = np.array([[0, 0, 5], [0, 5, 199], [0, 3, 130]])
+    oo, ll = fp8_attention_emulation(q8, k8, v8, sq, sk, sv, 0.125, causal, rows=rows)
+    for i, (b, h, n) in enumerate(rows):
+        np.testing.assert_array_equal(oo[i], o[b, n, h])
+        np.testing.assert_array_equal(ll[i], l[b, h, n])
