@@ -10,6 +10,8 @@ Entry points (same names as the C ABI):
   attn_fwd_bf16(q, k, v, causal=False, softmax_scale=None) -> (o, lse)
   blockquant_hadamard(x, signs=None, block_rows=128) -> (x8, scale)
   attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal=False, softmax_scale=None) -> (o, lse)
+  attn_fwd_bf16_gqa / attn_fwd_fp8_gqa: the same with K/V (and their scales) on
+    H_kv heads, H a multiple of H_kv (grouped-query / multi-query attention).
 Tensors are BSHD (batch, seqlen, heads, head_dim), contiguous, on a HIP device.
 """
 from __future__ import annotations
@@ -30,6 +32,8 @@ _c_float = ctypes.c_float
 SIGNATURES = {
     "attn_fwd_bf16": [_c_void_p] * 5 + [_c_int] * 5 + [_c_float, _c_void_p],
     "attn_fwd_fp8": [_c_void_p] * 8 + [_c_int] * 5 + [_c_float, _c_void_p],
+    "attn_fwd_bf16_gqa": [_c_void_p] * 5 + [_c_int] * 6 + [_c_float, _c_void_p],
+    "attn_fwd_fp8_gqa": [_c_void_p] * 8 + [_c_int] * 6 + [_c_float, _c_void_p],
     "blockquant_hadamard": [_c_void_p] * 4 + [_c_int] * 5 + [_c_void_p],
     "exattn_strerror": [_c_int],
     "exattn_abi_version": [],
@@ -89,21 +93,48 @@ def _call(fn: str, *args) -> None:
         raise ExattnError(fn, rc)
 
 
-def attn_fwd_bf16(q, k, v, causal: bool = False, softmax_scale: float | None = None,
-                  out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
-    """O = softmax(scale Q K^T [causal]) V in bf16; returns (O bf16 BSHD, LSE fp32 [B,H,N])."""
+def _kv_heads(name: str, q_shape, k_shape, v_shape, grouped: bool) -> int:
+    """K/V head count after checking the K/V shapes against Q's [B, N, H, d]."""
+    B, N, H, d = q_shape
+    if k_shape != v_shape:
+        raise ValueError(f"{name}: k and v must have the same shape")
+    if (k_shape[0], k_shape[1], k_shape[3]) != (B, N, d):
+        raise ValueError(f"{name}: k, v must be [B, N, H_kv, d] with q's B, N, d")
+    Hkv = k_shape[2]
+    if not grouped and Hkv != H:
+        raise ValueError(f"{name}: q, k, v must have the same shape (use {name}_gqa for H_kv < H)")
+    if Hkv < 1 or H % Hkv:
+        raise ValueError(f"{name}: H = {H} must be a multiple of H_kv = {Hkv}")
+    return Hkv
+
+
+def _bf16(fn, q, k, v, causal, softmax_scale, out, lse):
     shape = _check_bshd("q", q, torch.bfloat16)
-    if _check_bshd("k", k, torch.bfloat16) != shape or _check_bshd("v", v, torch.bfloat16) != shape:
-        raise ValueError("q, k, v must have the same shape")
+    Hkv = _kv_heads("attn_fwd_bf16", shape, _check_bshd("k", k, torch.bfloat16),
+                    _check_bshd("v", v, torch.bfloat16), fn.endswith("_gqa"))
     B, N, H, d = shape
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    _call("attn_fwd_bf16", q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-          B, H, N, d, int(bool(causal)), scale, _stream_ptr(q))
+    heads = (H, Hkv) if fn.endswith("_gqa") else (H,)
+    _call(fn, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+          B, *heads, N, d, int(bool(causal)), scale, _stream_ptr(q))
     return out, lse
+
+
+def attn_fwd_bf16(q, k, v, causal: bool = False, softmax_scale: float | None = None,
+                  out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """O = softmax(scale Q K^T [causal]) V in bf16; returns (O bf16 BSHD, LSE fp32 [B,H,N])."""
+    return _bf16("attn_fwd_bf16", q, k, v, causal, softmax_scale, out, lse)
+
+
+def attn_fwd_bf16_gqa(q, k, v, causal: bool = False, softmax_scale: float | None = None,
+                      out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """attn_fwd_bf16 with K/V on H_kv heads ([B, N, H_kv, d]); query head h uses
+    K/V head h // (H // H_kv)."""
+    return _bf16("attn_fwd_bf16_gqa", q, k, v, causal, softmax_scale, out, lse)
 
 
 def blockquant_hadamard(x, signs: torch.Tensor | None = None, block_rows: int = 128,
@@ -127,29 +158,44 @@ def blockquant_hadamard(x, signs: torch.Tensor | None = None, block_rows: int = 
     return out, scale
 
 
-def attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False,
-                 softmax_scale: float | None = None, out: torch.Tensor | None = None,
-                 lse: torch.Tensor | None = None):
-    """FP8 attention on e4m3 codes (uint8 or float8_e4m3fn) with block scales."""
+def _fp8(fn, q8, k8, v8, q_scale, k_scale, v_scale, causal, softmax_scale, out, lse):
     codes = (torch.uint8, torch.float8_e4m3fn)
     shape = _check_bshd("q8", q8, codes)
-    if _check_bshd("k8", k8, codes) != shape or _check_bshd("v8", v8, codes) != shape:
-        raise ValueError("q8, k8, v8 must have the same shape")
+    Hkv = _kv_heads("attn_fwd_fp8", shape, _check_bshd("k8", k8, codes),
+                    _check_bshd("v8", v8, codes), fn.endswith("_gqa"))
     B, N, H, d = shape
     nsb = (N + 127) // 128
-    for name, s in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
-        if s.dtype != torch.float32 or tuple(s.shape) != (B, H, nsb) or not s.is_contiguous():
-            raise ValueError(f"{name} must be contiguous float32 [B, H, ceil(N/128)]")
+    for name, s, h in (("q_scale", q_scale, H), ("k_scale", k_scale, Hkv), ("v_scale", v_scale, Hkv)):
+        if s.dtype != torch.float32 or tuple(s.shape) != (B, h, nsb) or not s.is_contiguous():
+            raise ValueError(f"{name} must be contiguous float32 [B, {h}, ceil(N/128)]")
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     if out is None:
         out = torch.empty((B, N, H, d), dtype=torch.bfloat16, device=q8.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
-    _call("attn_fwd_fp8", q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), q_scale.data_ptr(),
-          k_scale.data_ptr(), v_scale.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+    heads = (H, Hkv) if fn.endswith("_gqa") else (H,)
+    _call(fn, q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), q_scale.data_ptr(),
+          k_scale.data_ptr(), v_scale.data_ptr(), out.data_ptr(), lse.data_ptr(), B, *heads, N, d,
           int(bool(causal)), scale, _stream_ptr(q8))
     return out, lse
 
 
-__all__ = ["attn_fwd_bf16", "attn_fwd_fp8", "blockquant_hadamard", "lib", "strerror",
+def attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False,
+                 softmax_scale: float | None = None, out: torch.Tensor | None = None,
+                 lse: torch.Tensor | None = None):
+    """FP8 attention on e4m3 codes (uint8 or float8_e4m3fn) with block scales."""
+    return _fp8("attn_fwd_fp8", q8, k8, v8, q_scale, k_scale, v_scale, causal, softmax_scale,
+                out, lse)
+
+
+def attn_fwd_fp8_gqa(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False,
+                     softmax_scale: float | None = None, out: torch.Tensor | None = None,
+                     lse: torch.Tensor | None = None):
+    """attn_fwd_fp8 with K/V codes [B, N, H_kv, d] and K/V scales [B, H_kv, ceil(N/128)]."""
+    return _fp8("attn_fwd_fp8_gqa", q8, k8, v8, q_scale, k_scale, v_scale, causal, softmax_scale,
+                out, lse)
+
+
+__all__ = ["attn_fwd_bf16", "attn_fwd_fp8", "attn_fwd_bf16_gqa", "attn_fwd_fp8_gqa",
+           "blockquant_hadamard", "lib", "strerror",
            "ExattnError", "LIB_PATH", "SIGNATURES"]

@@ -34,19 +34,24 @@ int check_shape(int B, int H, int N, int d, int elt) {
 
 bool good_scale(float s) { return isfinite(s) && s > 0.f; }
 
+// K/V head count: at least 1 (for H > 0) and dividing H.
+bool good_heads(int H, int H_kv) { return H_kv > 0 ? H % H_kv == 0 : H == 0 && H_kv == 0; }
+
 int hip_status(hipError_t e) { return e == hipSuccess ? EXATTN_OK : EXATTN_ERR_HIP; }
 
 }  // namespace
 
 extern "C" {
 
-int exattn_abi_version(void) { return 1; }
+int exattn_abi_version(void) { return 2; }
 
 const char* exattn_strerror(int code) {
   switch (code) {
     case EXATTN_OK: return "success";
     case EXATTN_ERR_NULL: return "a required pointer is NULL";
-    case EXATTN_ERR_SHAPE: return "unsupported shape (negative size, d not in {64,128}, or too large)";
+    case EXATTN_ERR_SHAPE:
+      return "unsupported shape (negative size, d not in {64,128}, too large, or H not a multiple "
+             "of H_kv)";
     case EXATTN_ERR_ALIGN: return "pointer not aligned (tensors 16 bytes, scales/LSE 4 bytes)";
     case EXATTN_ERR_VALUE: return "invalid value (softmax_scale, causal, block_rows, or aliasing output)";
     case EXATTN_ERR_HIP: return "HIP error (no device or kernel launch failed)";
@@ -54,31 +59,42 @@ const char* exattn_strerror(int code) {
   }
 }
 
-int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                  int N, int d, int causal, float softmax_scale, void* stream) {
+int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                      int H, int H_kv, int N, int d, int causal, float softmax_scale,
+                      void* stream) {
   int rc = check_shape(B, H, N, d, 2);
   if (rc) return rc;
+  if (!good_heads(H, H_kv)) return EXATTN_ERR_SHAPE;
   if ((causal != 0 && causal != 1) || !good_scale(softmax_scale)) return EXATTN_ERR_VALUE;
   const int64_t bytes = (int64_t)B * N * H * d * 2;
+  const int64_t kv_bytes = (int64_t)B * N * H_kv * d * 2;
   if (bytes == 0) return EXATTN_OK;
   if (!q || !k || !v || !o) return EXATTN_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       (lse && !aligned(lse, 4)))
     return EXATTN_ERR_ALIGN;
-  if (overlap(o, bytes, q, bytes) || overlap(o, bytes, k, bytes) || overlap(o, bytes, v, bytes))
+  if (overlap(o, bytes, q, bytes) || overlap(o, bytes, k, kv_bytes) ||
+      overlap(o, bytes, v, kv_bytes))
     return EXATTN_ERR_VALUE;
   if (lse && overlap(lse, (int64_t)B * H * N * 4, o, bytes)) return EXATTN_ERR_VALUE;
-  return hip_status(exattn::launch_attn_fwd_bf16(q, k, v, o, lse, B, H, N, d, causal != 0,
+  return hip_status(exattn::launch_attn_fwd_bf16(q, k, v, o, lse, B, H, H_kv, N, d, causal != 0,
                                                  softmax_scale, (hipStream_t)stream));
 }
 
-int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_scale,
-                 const float* k_scale, const float* v_scale, void* o, float* lse, int B, int H,
-                 int N, int d, int causal, float softmax_scale, void* stream) {
+int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                  int N, int d, int causal, float softmax_scale, void* stream) {
+  return attn_fwd_bf16_gqa(q, k, v, o, lse, B, H, H, N, d, causal, softmax_scale, stream);
+}
+
+int attn_fwd_fp8_gqa(const void* q8, const void* k8, const void* v8, const float* q_scale,
+                     const float* k_scale, const float* v_scale, void* o, float* lse, int B, int H,
+                     int H_kv, int N, int d, int causal, float softmax_scale, void* stream) {
   int rc = check_shape(B, H, N, d, 1);
   if (rc) return rc;
+  if (!good_heads(H, H_kv)) return EXATTN_ERR_SHAPE;
   if ((causal != 0 && causal != 1) || !good_scale(softmax_scale)) return EXATTN_ERR_VALUE;
   const int64_t in_bytes = (int64_t)B * N * H * d;
+  const int64_t kv_bytes = (int64_t)B * N * H_kv * d;
   if (in_bytes == 0) return EXATTN_OK;
   if (!q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale || !o) return EXATTN_ERR_NULL;
   if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8, 16) || !aligned(o, 16) ||
@@ -86,13 +102,20 @@ int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_
       (lse && !aligned(lse, 4)))
     return EXATTN_ERR_ALIGN;
   const int64_t out_bytes = 2 * in_bytes;
-  if (overlap(o, out_bytes, q8, in_bytes) || overlap(o, out_bytes, k8, in_bytes) ||
-      overlap(o, out_bytes, v8, in_bytes))
+  if (overlap(o, out_bytes, q8, in_bytes) || overlap(o, out_bytes, k8, kv_bytes) ||
+      overlap(o, out_bytes, v8, kv_bytes))
     return EXATTN_ERR_VALUE;
   if (lse && overlap(lse, (int64_t)B * H * N * 4, o, out_bytes)) return EXATTN_ERR_VALUE;
   return hip_status(exattn::launch_attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B,
-                                                H, N, d, causal != 0, softmax_scale,
+                                                H, H_kv, N, d, causal != 0, softmax_scale,
                                                 (hipStream_t)stream));
+}
+
+int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_scale,
+                 const float* k_scale, const float* v_scale, void* o, float* lse, int B, int H,
+                 int N, int d, int causal, float softmax_scale, void* stream) {
+  return attn_fwd_fp8_gqa(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, H, N, d, causal,
+                          softmax_scale, stream);
 }
 
 int blockquant_hadamard(const void* x, void* x8, float* scale, const float* signs, int B, int H,

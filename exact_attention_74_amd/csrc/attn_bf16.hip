@@ -242,8 +242,8 @@ __device__ __forceinline__ void tile_compute(const char* smem, const uint32_t (&
 template <int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    __bf16* __restrict__ O, float* __restrict__ LSE, int H, int N, float scale_log2, int nqb,
-    int xcd_remap) {
+    __bf16* __restrict__ O, float* __restrict__ LSE, int H, int Hkv, int N, float scale_log2,
+    int nqb, int xcd_remap) {
   using G = Geo<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * G::STAGE];
 
@@ -262,6 +262,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_bf16_kernel(
   const int h = bh - b * H;
   const int64_t rs = (int64_t)H * D;
   const int64_t head_off = ((int64_t)b * N * H + h) * D;
+  // Grouped-query attention: H / Hkv consecutive query heads read one K/V head.
+  const int64_t rs_kv = (int64_t)Hkv * D;
+  const int64_t kv_off = ((int64_t)b * N * Hkv + h / (H / Hkv)) * D;
 
   constexpr int kBR = 32 * NW;                       // query rows per workgroup
   constexpr int LOADS = G::TILE / (1024 * NW);        // 1 KB copies per wave per tile
@@ -278,12 +281,12 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_bf16_kernel(
 
   // Buffer descriptors over this head's K and V rows; row n >= N is out of
   // range (reads return 0).
-  const uint32_t nbytes = (uint32_t)(((int64_t)(N - 1) * rs + D) * 2);
+  const uint32_t nbytes = (uint32_t)(((int64_t)(N - 1) * rs_kv + D) * 2);
   const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(K + head_off), (short)0, nbytes, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(K + kv_off), (short)0, nbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(V + head_off), (short)0, nbytes, 0x00020000);
-  const uint32_t row_bytes = (uint32_t)(rs * 2);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(V + kv_off), (short)0, nbytes, 0x00020000);
+  const uint32_t row_bytes = (uint32_t)(rs_kv * 2);
 
   // Per-lane global byte offsets of the chunks this lane deposits into LDS.
   uint32_t voff_k[LOADS], voff_v[LOADS];
@@ -378,14 +381,14 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_bf16_kernel(
 
 template <int D, bool CAUSAL, int NW>
 hipError_t launch_nw(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                     int N, float scale, hipStream_t stream) {
+                     int Hkv, int N, float scale, hipStream_t stream) {
   constexpr int kBR = 32 * NW;
   const int nqb = (N + kBR - 1) / kBR;
   const int64_t grid = (int64_t)B * H * nqb;
   const int remap = (grid % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, NW>), dim3((unsigned)grid), dim3(64 * NW), 0,
                      stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse,
-                     H, N, scale * kLog2e, nqb, remap);
+                     H, Hkv, N, scale * kLog2e, nqb, remap);
   return hipGetLastError();
 }
 
@@ -395,22 +398,22 @@ hipError_t launch_nw(const void* q, const void* k, const void* v, void* o, float
 // N <= 4096 / 8192 causal.
 template <int D, bool CAUSAL>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                  int N, float scale, hipStream_t stream) {
+                  int Hkv, int N, float scale, hipStream_t stream) {
   const int small_n = (CAUSAL ? 4096 : 1024) * (128 / D);
-  if (N <= small_n) return launch_nw<D, CAUSAL, 4>(q, k, v, o, lse, B, H, N, scale, stream);
-  return launch_nw<D, CAUSAL, 8>(q, k, v, o, lse, B, H, N, scale, stream);
+  if (N <= small_n) return launch_nw<D, CAUSAL, 4>(q, k, v, o, lse, B, H, Hkv, N, scale, stream);
+  return launch_nw<D, CAUSAL, 8>(q, k, v, o, lse, B, H, Hkv, N, scale, stream);
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                                int B, int H, int N, int d, bool causal, float softmax_scale,
-                                hipStream_t stream) {
+                                int B, int H, int Hkv, int N, int d, bool causal,
+                                float softmax_scale, hipStream_t stream) {
   if (d == 128)
-    return causal ? launch<128, true>(q, k, v, o, lse, B, H, N, softmax_scale, stream)
-                  : launch<128, false>(q, k, v, o, lse, B, H, N, softmax_scale, stream);
-  return causal ? launch<64, true>(q, k, v, o, lse, B, H, N, softmax_scale, stream)
-                : launch<64, false>(q, k, v, o, lse, B, H, N, softmax_scale, stream);
+    return causal ? launch<128, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream)
+                  : launch<128, false>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream);
+  return causal ? launch<64, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream)
+                : launch<64, false>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream);
 }
 
 }  // namespace exattn

@@ -105,8 +105,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
     const float* __restrict__ SQ, const float* __restrict__ SK, const float* __restrict__ SV,
-    __bf16* __restrict__ O, float* __restrict__ LSE, int H, int N, float scale_log2, int nqb,
-    int xcd_remap) {
+    __bf16* __restrict__ O, float* __restrict__ LSE, int H, int Hkv, int N, float scale_log2,
+    int nqb, int xcd_remap) {
   using G = Geo8<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * G::STAGE];
 
@@ -125,9 +125,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   const int h = bh - b * H;
   const int64_t rs = (int64_t)H * D;
   const int64_t head_off = ((int64_t)b * N * H + h) * D;
+  // Grouped-query attention: H / Hkv consecutive query heads read one K/V head.
+  const int bhk = b * Hkv + h / (H / Hkv);
+  const int64_t rs_kv = (int64_t)Hkv * D;
+  const int64_t kv_off = ((int64_t)b * N * Hkv + h / (H / Hkv)) * D;
   const int nsb = (N + kQB - 1) / kQB;
-  const float* sk_bh = SK + (int64_t)bh * nsb;
-  const float* sv_bh = SV + (int64_t)bh * nsb;
+  const float* sk_bh = SK + (int64_t)bhk * nsb;
+  const float* sv_bh = SV + (int64_t)bhk * nsb;
 
   const int q0 = qblk * kBR + wave * 32;
   const int qi = q0 + li;
@@ -142,12 +146,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     qf[t] = (qi < N) ? *(const i32x8*)(Q + head_off + (int64_t)qi * rs + 64 * t + 32 * hh) : z;
   }
 
-  const uint32_t nbytes = (uint32_t)((int64_t)(N - 1) * rs + D);
+  const uint32_t nbytes = (uint32_t)((int64_t)(N - 1) * rs_kv + D);
   const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(K + head_off), (short)0, nbytes, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(K + kv_off), (short)0, nbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(V + head_off), (short)0, nbytes, 0x00020000);
-  const uint32_t row_bytes = (uint32_t)rs;
+      __builtin_amdgcn_make_buffer_rsrc((void*)(V + kv_off), (short)0, nbytes, 0x00020000);
+  const uint32_t row_bytes = (uint32_t)rs_kv;
   uint32_t voff_k[G::LOADS], voff_v[G::LOADS];
 #pragma unroll
   for (int i = 0; i < G::LOADS; ++i) {
@@ -329,14 +333,14 @@ _Pragma("unroll")                                                               
 
 template <int D, bool CAUSAL>
 hipError_t launch(const void* q8, const void* k8, const void* v8, const float* sq, const float* sk,
-                  const float* sv, void* o, float* lse, int B, int H, int N, float scale,
-                  hipStream_t stream) {
+                  const float* sv, void* o, float* lse, int B, int H, int Hkv, int N,
+                  float scale, hipStream_t stream) {
   const int nqb = (N + kBR - 1) / kBR;
   const int64_t grid = (int64_t)B * H * nqb;
   const int remap = (grid % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0,
                      stream, (const uint8_t*)q8, (const uint8_t*)k8, (const uint8_t*)v8, sq, sk, sv,
-                     (__bf16*)o, lse, H, N, scale * kLog2e, nqb, remap);
+                     (__bf16*)o, lse, H, Hkv, N, scale * kLog2e, nqb, remap);
   return hipGetLastError();
 }
 
@@ -344,12 +348,13 @@ hipError_t launch(const void* q8, const void* k8, const void* v8, const float* s
 
 hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* sq,
                                const float* sk, const float* sv, void* o, float* lse, int B, int H,
-                               int N, int d, bool causal, float softmax_scale, hipStream_t stream) {
+                               int Hkv, int N, int d, bool causal, float softmax_scale,
+                               hipStream_t stream) {
   if (d == 128)
-    return causal ? launch<128, true>(q8, k8, v8, sq, sk, sv, o, lse, B, H, N, softmax_scale, stream)
-                  : launch<128, false>(q8, k8, v8, sq, sk, sv, o, lse, B, H, N, softmax_scale, stream);
-  return causal ? launch<64, true>(q8, k8, v8, sq, sk, sv, o, lse, B, H, N, softmax_scale, stream)
-                : launch<64, false>(q8, k8, v8, sq, sk, sv, o, lse, B, H, N, softmax_scale, stream);
+    return causal ? launch<128, true>(q8, k8, v8, sq, sk, sv, o, lse, B, H, Hkv, N, softmax_scale, stream)
+                  : launch<128, false>(q8, k8, v8, sq, sk, sv, o, lse, B, H, Hkv, N, softmax_scale, stream);
+  return causal ? launch<64, true>(q8, k8, v8, sq, sk, sv, o, lse, B, H, Hkv, N, softmax_scale, stream)
+                : launch<64, false>(q8, k8, v8, sq, sk, sv, o, lse, B, H, Hkv, N, softmax_scale, stream);
 }
 
 }  // namespace exattn

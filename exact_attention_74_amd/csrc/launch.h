@@ -7,13 +7,15 @@
 
 namespace exattn {
 
+// Hkv: K/V heads (H a multiple of it); query head h reads K/V head h / (H / Hkv).
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                                int B, int H, int N, int d, bool causal, float softmax_scale,
-                                hipStream_t stream);
+                                int B, int H, int Hkv, int N, int d, bool causal,
+                                float softmax_scale, hipStream_t stream);
 
 hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* sq,
                                const float* sk, const float* sv, void* o, float* lse, int B, int H,
-                               int N, int d, bool causal, float softmax_scale, hipStream_t stream);
+                               int Hkv, int N, int d, bool causal, float softmax_scale,
+                               hipStream_t stream);
 
 hipError_t launch_blockquant(const void* x, void* x8, float* scale, const float* signs, int B, int H,
                              int N, int d, int block_rows, hipStream_t stream);

@@ -89,6 +89,27 @@ int attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
                  int B, int H, int N, int d, int causal, float softmax_scale, void* stream);
 
 /*
+ * Grouped-query / multi-query variants (FlashAttention-3 report, section 3.4:
+ * MQA and GQA by FA-2's index mapping, so K/V are not duplicated in HBM).
+ *   k, v (k8, v8)   BSHD with H_kv heads: [B, N, H_kv, d].
+ *   k_scale, v_scale   fp32 [B, H_kv, ceil(N/128)].
+ *   H_kv         K/V heads, >= 1, dividing H; query head h attends with K/V
+ *                head h / (H / H_kv).  H_kv = H is plain multi-head attention,
+ *                H_kv = 1 multi-query attention.
+ * Everything else, outputs included (H heads), as in attn_fwd_bf16 and
+ * attn_fwd_fp8; those two are these with H_kv = H.  H not a multiple of H_kv
+ * (or H_kv < 1 with H > 0) returns EXATTN_ERR_SHAPE.
+ */
+int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int H_kv, int N, int d, int causal, float softmax_scale,
+                      void* stream);
+int attn_fwd_fp8_gqa(const void* q8, const void* k8, const void* v8,
+                     const float* q_scale, const float* k_scale, const float* v_scale,
+                     void* o, float* lse,
+                     int B, int H, int H_kv, int N, int d, int causal, float softmax_scale,
+                     void* stream);
+
+/*
  * FP8 pre-pass: optional incoherent rotation, then block quantisation to e4m3
  * (FlashAttention-3 report, sections 2.2 and 3.3).
  *   x        bfloat16 BSHD input.

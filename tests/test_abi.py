@@ -30,13 +30,13 @@ def _codes():
 
 def test_library_builds_and_loads():
     assert os.path.exists(ea.LIB_PATH)
-    assert ea.lib().exattn_abi_version() == 1
+    assert ea.lib().exattn_abi_version() == 2
 
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert set(names) == {"attn_fwd_bf16", "attn_fwd_fp8", "blockquant_hadamard",
-                          "exattn_strerror", "exattn_abi_version"}
+    assert set(names) == {"attn_fwd_bf16", "attn_fwd_fp8", "attn_fwd_bf16_gqa", "attn_fwd_fp8_gqa",
+                          "blockquant_hadamard", "exattn_strerror", "exattn_abi_version"}
     raw = ctypes.CDLL(ea.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -64,11 +64,24 @@ def _fp8(q=P, k=P + P2, v=P + 2 * P2, sq=P + 3 * P2, sk=P + 4 * P2, sv=P + 5 * P
     return ea.lib().attn_fwd_fp8(q, k, v, sq, sk, sv, o, lse, B, H, N, d, causal, scale, None)
 
 
+def _bf16g(q=P, k=P + P2, v=P + 2 * P2, o=P + 3 * P2, lse=P + 4 * P2, B=1, H=2, Hkv=None, N=256,
+           d=64, causal=0, scale=0.125):
+    Hkv = H if Hkv is None else Hkv
+    return ea.lib().attn_fwd_bf16_gqa(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale, None)
+
+
+def _fp8g(q=P, k=P + P2, v=P + 2 * P2, sq=P + 3 * P2, sk=P + 4 * P2, sv=P + 5 * P2, o=P + 6 * P2,
+          lse=P + 7 * P2, B=1, H=2, Hkv=None, N=256, d=64, causal=0, scale=0.125):
+    Hkv = H if Hkv is None else Hkv
+    return ea.lib().attn_fwd_fp8_gqa(q, k, v, sq, sk, sv, o, lse, B, H, Hkv, N, d, causal, scale,
+                                     None)
+
+
 def _bq(x=P, x8=P + P2, s=P + 2 * P2, signs=None, B=1, H=2, N=256, d=64, br=128):
     return ea.lib().blockquant_hadamard(x, x8, s, signs, B, H, N, d, br, None)
 
 
-@pytest.mark.parametrize("fn", [_bf16, _fp8])
+@pytest.mark.parametrize("fn", [_bf16, _fp8, _bf16g, _fp8g])
 def test_attention_validation(fn):
     assert fn(q=None) == ea.ERR_NULL
     assert fn(o=None) == ea.ERR_NULL
@@ -94,6 +107,20 @@ def test_attention_validation(fn):
     assert fn(H=0) == 0
     assert fn(B=0, q=None, o=None) == 0
     assert fn(N=0, d=96) == ea.ERR_SHAPE
+
+
+@pytest.mark.parametrize("fn", [_bf16g, _fp8g])
+def test_gqa_head_counts(fn):
+    assert fn(H=4, Hkv=3) == ea.ERR_SHAPE   # H not a multiple of H_kv
+    assert fn(H=2, Hkv=4) == ea.ERR_SHAPE   # more K/V heads than query heads
+    assert fn(H=4, Hkv=0) == ea.ERR_SHAPE
+    assert fn(H=4, Hkv=-2) == ea.ERR_SHAPE
+    assert fn(H=0, Hkv=0) == 0              # empty problem
+    assert fn(H=8, Hkv=2, q=None) == ea.ERR_NULL
+    assert fn(H=8, Hkv=2, B=0) == 0
+    assert fn(H=8, Hkv=1, q=P + 8) == ea.ERR_ALIGN
+    # output aliasing the (smaller) K tensor
+    assert fn(H=8, Hkv=2, o=P + P2 + 64) == ea.ERR_VALUE
 
 
 def test_fp8_scale_pointers_required():

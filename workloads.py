@@ -106,6 +106,15 @@ def gen_qkv(w: Workload) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
     return out[0], out[1], out[2]
 
 
+def gen_qkv_gqa(B: int, N: int, H: int, Hkv: int, d: int, seed: int, dist: str = "normal"):
+    """Q on H heads and K, V on Hkv heads (BSHD float32) for grouped-query
+    attention, drawn like ``gen_qkv``: Q from ``seed``, K and V from the next
+    draws of the same stream."""
+    q = gen_qkv(Workload("q", B, H, N, d, False, seed=seed, dist=dist))[0]
+    _, k, v = gen_qkv(Workload("kv", B, Hkv, N, d, False, seed=seed + 1, dist=dist))
+    return q, k, v
+
+
 def gen_signs(d: int, seed: int = SIGNS_SEED) -> np.ndarray:
     """d random signs (+1/-1, float32) for the incoherent-processing diagonal."""
     rng = np.random.default_rng(seed)
