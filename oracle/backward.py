@@ -1,0 +1,76 @@
+"""Gradients of exact attention, fp64: the definition (test infrastructure).
+
+Test infrastructure only (see the package docstring).
+
+The backward pass of [FA3-report] section 3.4 keeps FA-2's strategy: it
+recomputes the score block from Q, K and the saved log-sum-exp instead of
+storing P, and does five matrix products per block (2.5 times the forward's
+two); [FA3-blog] section 5.4 is the reminder that the softmax statistics must
+be kept (or recomputed) for it.  What is computed is the plain derivative of
+the forward definition.  For one (b, h), with O = P V and the loss gradient
+dO:
+
+    P    = softmax(scale Q K^T [causal])        (exactly, from LSE)
+    D_i  = sum_c dO[i, c] O[i, c]
+    dV   = P^T dO
+    dP   = dO V^T
+    dS   = P * (dP - D)                          (elementwise; D per row)
+    dQ   = scale dS K
+    dK   = scale dS^T Q
+
+(dS is the gradient with respect to the scores S = scale Q K^T that enter
+the softmax; its rows sum to zero because the rows of P sum to one.)
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import _heads
+
+
+def _probs(qh, kh, scale, causal):
+    s = scale * (qh @ kh.T)
+    if causal:
+        n, m = s.shape
+        s[np.arange(m)[None, :] > np.arange(n)[:, None]] = -np.inf
+    mx = np.max(s, axis=1, keepdims=True)
+    e = np.exp(s - mx)
+    return e / np.sum(e, axis=1, keepdims=True)
+
+
+def attention_backward(q, k, v, do, scale: float, causal: bool):
+    """(dQ, dK, dV) as fp64 BSHD arrays for inputs q, k, v and output gradient
+    do (all BSHD, same shape)."""
+    qh, kh, vh, doh = _heads(q), _heads(k), _heads(v), _heads(do)
+    B, H, N, d = qh.shape
+    dq = np.empty_like(qh)
+    dk = np.empty_like(kh)
+    dv = np.empty_like(vh)
+    for b in range(B):
+        for h in range(H):
+            p = _probs(qh[b, h], kh[b, h], scale, causal)
+            o = p @ vh[b, h]
+            dd = np.sum(doh[b, h] * o, axis=1)
+            dv[b, h] = p.T @ doh[b, h]
+            dp = doh[b, h] @ vh[b, h].T
+            ds = p * (dp - dd[:, None])
+            dq[b, h] = scale * (ds @ kh[b, h])
+            dk[b, h] = scale * (ds.T @ qh[b, h])
+    back = lambda x: np.transpose(x, (0, 2, 1, 3))  # noqa: E731
+    return back(dq), back(dk), back(dv)
+
+
+def attention_backward_heads(q, k, v, do, scale: float, causal: bool, heads):
+    """The same for selected (b, h) pairs only: ``heads`` is an int array
+    [R, 2].  Returns fp64 arrays [R, N, d] for dQ, dK, dV (large workloads are
+    checked on a few whole heads: every key's gradient needs every query)."""
+    q, k, v, do = (np.asarray(x) for x in (q, k, v, do))
+    heads = np.asarray(heads, np.int64)
+    R, N, d = heads.shape[0], q.shape[1], q.shape[3]
+    out = [np.empty((R, N, d)) for _ in range(3)]
+    for r, (b, h) in enumerate(heads):
+        sl = lambda x: np.asarray(x[b:b + 1, :, h:h + 1, :], np.float64)  # noqa: E731
+        g = attention_backward(sl(q), sl(k), sl(v), sl(do), scale, causal)
+        for t in range(3):
+            out[t][r] = g[t][0, :, 0, :]
+    return tuple(out)
