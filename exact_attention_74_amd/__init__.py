@@ -12,6 +12,7 @@ Entry points (same names as the C ABI):
   attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal=False, softmax_scale=None) -> (o, lse)
   attn_fwd_bf16_gqa / attn_fwd_fp8_gqa: the same with K/V (and their scales) on
     H_kv heads, H a multiple of H_kv (grouped-query / multi-query attention).
+  attn_bwd_bf16(q, k, v, o, lse, do, causal=False, softmax_scale=None) -> (dq, dk, dv)
 Tensors are BSHD (batch, seqlen, heads, head_dim), contiguous, on a HIP device.
 """
 from __future__ import annotations
@@ -34,11 +35,13 @@ SIGNATURES = {
     "attn_fwd_fp8": [_c_void_p] * 8 + [_c_int] * 5 + [_c_float, _c_void_p],
     "attn_fwd_bf16_gqa": [_c_void_p] * 5 + [_c_int] * 6 + [_c_float, _c_void_p],
     "attn_fwd_fp8_gqa": [_c_void_p] * 8 + [_c_int] * 6 + [_c_float, _c_void_p],
+    "attn_bwd_bf16": [_c_void_p] * 10 + [_c_int] * 5 + [_c_float, _c_void_p],
+    "attn_bwd_bf16_workspace_bytes": [_c_int] * 3,
     "blockquant_hadamard": [_c_void_p] * 4 + [_c_int] * 5 + [_c_void_p],
     "exattn_strerror": [_c_int],
     "exattn_abi_version": [],
 }
-RESTYPES = {"exattn_strerror": ctypes.c_char_p}
+RESTYPES = {"exattn_strerror": ctypes.c_char_p, "attn_bwd_bf16_workspace_bytes": ctypes.c_longlong}
 
 ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_VALUE, ERR_HIP = -1, -2, -3, -4, -5
 
@@ -196,6 +199,41 @@ def attn_fwd_fp8_gqa(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False
                 out, lse)
 
 
-__all__ = ["attn_fwd_bf16", "attn_fwd_fp8", "attn_fwd_bf16_gqa", "attn_fwd_fp8_gqa",
+def attn_bwd_bf16(q, k, v, o, lse, do, causal: bool = False, softmax_scale: float | None = None,
+                  dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
+                  dv: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Gradients (dQ, dK, dV) of attn_fwd_bf16 given its output ``o``, its LSE and
+    the output gradient ``do`` (all bf16 BSHD except the fp32 [B, H, N] LSE).
+
+    ``workspace``: optional float32 device tensor of at least
+    attn_bwd_bf16_workspace_bytes(B, H, N) bytes; allocated here if omitted.
+    """
+    shape = _check_bshd("q", q, torch.bfloat16)
+    for name, t in (("k", k), ("v", v), ("o", o), ("do", do)):
+        if _check_bshd(name, t, torch.bfloat16) != shape:
+            raise ValueError(f"{name} must have q's shape")
+    B, N, H, d = shape
+    if (not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32
+            or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    nbytes = lib().attn_bwd_bf16_workspace_bytes(B, H, N)
+    if nbytes < 0:
+        raise ExattnError("attn_bwd_bf16_workspace_bytes", nbytes)
+    if workspace is None:
+        workspace = torch.empty(max(1, nbytes // 4), dtype=torch.float32, device=q.device)
+    elif (workspace.dtype != torch.float32 or workspace.device != q.device
+          or workspace.numel() * 4 < nbytes or not workspace.is_contiguous()):
+        raise ValueError(f"workspace must be a contiguous float32 tensor of >= {nbytes} bytes")
+    _call("attn_bwd_bf16", q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+          lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+          B, H, N, d, int(bool(causal)), scale, _stream_ptr(q))
+    return dq, dk, dv
+
+
+__all__ = ["attn_fwd_bf16", "attn_fwd_fp8", "attn_fwd_bf16_gqa", "attn_fwd_fp8_gqa", "attn_bwd_bf16",
            "blockquant_hadamard", "lib", "strerror",
            "ExattnError", "LIB_PATH", "SIGNATURES"]

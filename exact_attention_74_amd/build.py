@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libexattn.so")
-SOURCES = ["attn_bf16.hip", "attn_fp8.hip", "blockquant.hip", "api.hip"]
+SOURCES = ["attn_bf16.hip", "attn_fp8.hip", "attn_bwd.hip", "blockquant.hip", "api.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.

@@ -43,7 +43,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? EXATTN_OK : EXATTN_ERR_H
 
 extern "C" {
 
-int exattn_abi_version(void) { return 2; }
+int exattn_abi_version(void) { return 3; }
 
 const char* exattn_strerror(int code) {
   switch (code) {
@@ -116,6 +116,45 @@ int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_
                  int N, int d, int causal, float softmax_scale, void* stream) {
   return attn_fwd_fp8_gqa(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, H, N, d, causal,
                           softmax_scale, stream);
+}
+
+long long attn_bwd_bf16_workspace_bytes(int B, int H, int N) {
+  if (B < 0 || H < 0 || N < 0) return EXATTN_ERR_SHAPE;
+  return 8LL * B * H * N;
+}
+
+int attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv, float* workspace, int B, int H,
+                  int N, int d, int causal, float softmax_scale, void* stream) {
+  int rc = check_shape(B, H, N, d, 2);
+  if (rc) return rc;
+  if ((causal != 0 && causal != 1) || !good_scale(softmax_scale)) return EXATTN_ERR_VALUE;
+  // the per-row prep kernel runs 16 rows per workgroup
+  if ((int64_t)B * N * H >= (int64_t(1) << 35)) return EXATTN_ERR_SHAPE;
+  const int64_t bytes = (int64_t)B * N * H * d * 2;
+  if (bytes == 0) return EXATTN_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
+    return EXATTN_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4) || !aligned(workspace, 4))
+    return EXATTN_ERR_ALIGN;
+  const int64_t lse_bytes = (int64_t)B * H * N * 4;
+  const int64_t ws_bytes = 2 * lse_bytes;
+  // Outputs and workspace must not overlap any input or each other.
+  const void* in[] = {q, k, v, o, dout, lse};
+  const int64_t in_n[] = {bytes, bytes, bytes, bytes, bytes, lse_bytes};
+  const void* out[] = {dq, dk, dv, workspace};
+  const int64_t out_n[] = {bytes, bytes, bytes, ws_bytes};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlap(out[i], out_n[i], in[j], in_n[j])) return EXATTN_ERR_VALUE;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(out[i], out_n[i], out[j], out_n[j])) return EXATTN_ERR_VALUE;
+  }
+  return hip_status(exattn::launch_attn_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, workspace, B,
+                                                 H, N, d, causal != 0, softmax_scale,
+                                                 (hipStream_t)stream));
 }
 
 int blockquant_hadamard(const void* x, void* x8, float* scale, const float* signs, int B, int H,

@@ -1,0 +1,527 @@
+// bf16 exact-attention gradients (dQ, dK, dV) for gfx950.
+//
+// The backward pass of the FlashAttention-3 report (section 3.4) keeps FA-2's
+// strategy: P is recomputed from Q, K and the saved log-sum-exp instead of
+// being stored.  Per (b, h), with O and dO the forward output and its
+// gradient:
+//   D_i = sum_c dO[i, c] O[i, c]
+//   P   = exp(scale Q K^T - LSE)            (causal: 0 for key > query)
+//   dV  = P^T dO
+//   dS  = P * (dO V^T - D)                   (D per query row)
+//   dQ  = scale dS K,   dK = scale dS^T Q
+//
+// Three kernels, launched in order on one stream:
+//   bwd_prep   D and LSE * log2(e) per query row, into the caller's workspace.
+//   bwd_dkdv   one workgroup per (b, h, 128 keys); each wave keeps its 32 keys'
+//              K^T and V^T in registers and streams 64-row Q and dO tiles
+//              (with their LSE and D) through LDS.  S = Q K^T and dP = dO V^T
+//              put one key on each MFMA column, so P and dS go straight from
+//              the accumulator into dV^T += dO^T P and dK^T += Q^T dS as the
+//              B operand, with dO^T and Q^T gathered by transposed LDS reads
+//              in the accumulator's row order (the forward's P^T relayout,
+//              with keys and queries exchanged).
+//   bwd_dq     one workgroup per (b, h, 128 queries), the forward kernel's
+//              layout: S^T = K Q^T and dP^T = V dO^T with Q^T, dO^T in
+//              registers, then dQ^T += K^T dS^T from transposed reads of K.
+// dQ gets its own kernel instead of fp32 atomics across key blocks: S and dP
+// are computed twice (seven matrix products instead of five) and every
+// result is deterministic.
+//
+// LDS tiles are 64 rows, copied by buffer_load ... lds (reads past the end of
+// the sequence return zeros) and double-buffered, as in the forward.  A tile
+// that is read both row-wise (ds_read_b128, an A operand) and transposed
+// (ds_read_b64_tr_b16) uses the chunk swizzle of the transposed reads, which
+// keeps the immediate offsets of both read patterns valid.
+#include "common.h"
+#include "launch.h"
+#include "lds_tile.h"
+
+namespace exattn {
+namespace {
+
+constexpr int kNWb = 4;           // waves per workgroup (both gradient kernels)
+constexpr int kRowsB = 32 * kNWb;  // query rows (dQ) or key rows (dK, dV) per workgroup
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Waits for every outstanding LDS read of this wave, passing the fragments
+// through so that no use of them is scheduled before the wait.
+template <int NF>
+__device__ __forceinline__ void lds_wait_frags(bf16x8 (&f)[NF]) {
+  static_assert(NF == 4 || NF == 8, "d = 64 or 128");
+  if constexpr (NF == 8)
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]),
+                   "+v"(f[6]), "+v"(f[7]));
+  else
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]));
+}
+
+__device__ __forceinline__ void lds_wait_f4(f32x4 (&a)[4], f32x4 (&b)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]),
+                 "+v"(b[2]), "+v"(b[3]));
+}
+
+template <int OFF>
+__device__ __forceinline__ f32x4 read_f4(uint32_t addr) {
+  f32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+// Transposed-read A-operand fragments for the 32 rows [32 J, 32 J + 32) of the
+// tile at LDS offset OFF: frag[T][e] covers rows 32 J + 16 T .. +15 (k) and
+// d-rows 32 e .. 32 e + 31, in the accumulator's row order (row 16 T +
+// 8 (s / 4) + 4 h + s % 4 in k-slot s of half-wave h).
+template <int D, int OFF, int J>
+__device__ __forceinline__ void read_tr_frags(const uint32_t (&taddr)[D / 32],
+                                              bf16x8 (&frag)[2][D / 32]) {
+  using G = Geo<D>;
+#pragma unroll
+  for (int e = 0; e < D / 32; ++e) {
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      constexpr int R0 = 32 * J;
+      const bf16x4 lo = T == 0 ? read_tr16<OFF + (R0 + 0) * G::RB>(taddr[e])
+                               : read_tr16<OFF + (R0 + 16) * G::RB>(taddr[e]);
+      const bf16x4 hi = T == 0 ? read_tr16<OFF + (R0 + 8) * G::RB>(taddr[e])
+                               : read_tr16<OFF + (R0 + 24) * G::RB>(taddr[e]);
+      frag[T][e] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  }
+}
+
+template <int NE>
+__device__ __forceinline__ void lds_wait_tr(bf16x8 (&f)[2][NE]) {
+  static_assert(NE == 4 || NE == 2, "d = 128 or 64");
+  if constexpr (NE == 4)
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(f[0][0]), "+v"(f[0][1]), "+v"(f[0][2]), "+v"(f[0][3]), "+v"(f[1][0]),
+                   "+v"(f[1][1]), "+v"(f[1][2]), "+v"(f[1][3]));
+  else
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[0][0]), "+v"(f[0][1]), "+v"(f[1][0]), "+v"(f[1][1]));
+}
+
+// LDS address of this lane's transposed-read source in a tile at LDS byte
+// address `base` (rows key-major, chunk swizzle swz_v): row 4 hv + j, chunk
+// 4 e + 2 (g % 2) + q / 2, half q % 2.
+template <int D>
+__device__ __forceinline__ void tr_addresses(uint32_t base, int lane, uint32_t (&taddr)[D / 32]) {
+  using G = Geo<D>;
+  const int src = lane & 15, g = lane >> 4;
+  const int j = src >> 2, q = src & 3, hv = g >> 1;
+  const int row = 4 * hv + j;
+#pragma unroll
+  for (int e = 0; e < D / 32; ++e) {
+    const int c = 4 * e + 2 * (g & 1) + (q >> 1);
+    taddr[e] = base + row * G::RB + ((c ^ G::swz_v(row)) * 16) + (q & 1) * 8;
+  }
+}
+
+// Global -> LDS copy offsets of this lane's chunks of a 64-row tile, for a
+// layout with chunk swizzle SWZ (0: swz_k, 1: swz_v).
+template <int D, int LOADS, int SWZ>
+__device__ __forceinline__ void copy_offsets(int wave, int lane, uint32_t row_bytes,
+                                             uint32_t (&voff)[LOADS]) {
+  using G = Geo<D>;
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int chunk = (wave * LOADS + i) * 64 + lane;
+    const int row = chunk / G::CPR, pos = chunk % G::CPR;
+    const int sw = SWZ ? G::swz_v(row) : G::swz_k(row);
+    voff[i] = row * row_bytes + (uint32_t)((pos ^ sw) * 16);
+  }
+}
+
+// Stores 32 rows x D of a transposed accumulator (lane = row li, d-values
+// 32 e + 8 (v / 4) + 4 h + v % 4 in element v) as bf16, times `mul`.
+template <int D>
+__device__ __forceinline__ void store_rows(__bf16* row_ptr, const f32x16 (&acc)[D / 32], float mul,
+                                           int hh) {
+#pragma unroll
+  for (int e = 0; e < D / 32; ++e)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      i32x2 pk;
+      pk[0] = (int)pack_bf16x2(acc[e][4 * g + 0] * mul, acc[e][4 * g + 1] * mul);
+      pk[1] = (int)pack_bf16x2(acc[e][4 * g + 2] * mul, acc[e][4 * g + 3] * mul);
+      *(i32x2*)(row_ptr + 32 * e + 8 * g + 4 * hh) = pk;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// D_i = sum_c dO[i, c] O[i, c] and LSE_i * log2(e); D / 8 lanes per row.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* __restrict__ O,
+                                                       const __bf16* __restrict__ dO,
+                                                       const float* __restrict__ LSE,
+                                                       float* __restrict__ Drow,
+                                                       float* __restrict__ L2, int H, int N,
+                                                       int64_t rows) {
+  constexpr int LPR = D / 8;
+  const int64_t r = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  const int c = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (r < rows) {
+    const bf16x8 o = *(const bf16x8*)(O + r * D + 8 * c);
+    const bf16x8 g = *(const bf16x8*)(dO + r * D + 8 * c);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = __builtin_fmaf((float)o[i], (float)g[i], acc);
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m, 64);
+  if (r < rows && c == 0) {
+    // BSHD row r = (b N + n) H + h  ->  [B, H, N] index (b H + h) N + n
+    const int64_t h = r % H, bn = r / H;
+    const int64_t n = bn % N, b = bn / N;
+    const int64_t idx = (b * H + h) * N + n;
+    Drow[idx] = acc;
+    L2[idx] = LSE[idx] * kLog2e;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: the forward kernel's layout.  Stage: K tile (swz_v: read as the S^T A
+// operand and transposed for K^T), V tile (swz_k: read as the dP^T A operand).
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64 * kNWb, 2) void bwd_dq_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const __bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Drow,
+    __bf16* __restrict__ dQ, int H, int N, float scale_log2, float scale, int nqb, int xcd_remap) {
+  using G = Geo<D>;
+  constexpr int NF = D / 16, NE = D / 32;
+  constexpr int LOADS = G::TILE / (1024 * kNWb);
+  __shared__ __attribute__((aligned(1024))) char smem[2 * G::STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31, hh = lane >> 5;
+  int L = blockIdx.x;
+  if (xcd_remap) L = (L & 7) * (gridDim.x >> 3) + (L >> 3);
+  const int qb_raw = L % nqb, bh = L / nqb;
+  const int qblk = CAUSAL ? (nqb - 1 - qb_raw) : qb_raw;  // heaviest causal blocks first
+  const int b = bh / H, h = bh - b * H;
+  const int64_t rs = (int64_t)H * D;
+  const int64_t head_off = ((int64_t)b * N * H + h) * D;
+  const int q0 = qblk * kRowsB + wave * 32;
+  const int qi = q0 + li;
+
+  // Q^T and dO^T as B operands: k-step t, half h -> dims 16 t + 8 h .. +7.
+  bf16x8 qf[NF], gf[NF];
+#pragma unroll
+  for (int t = 0; t < NF; ++t) {
+    const bf16x8 z = {};
+    qf[t] = qi < N ? *(const bf16x8*)(Q + head_off + (int64_t)qi * rs + 16 * t + 8 * hh) : z;
+    gf[t] = qi < N ? *(const bf16x8*)(dO + head_off + (int64_t)qi * rs + 16 * t + 8 * hh) : z;
+  }
+  const float lse2 = qi < N ? L2[(int64_t)bh * N + qi] : 0.f;
+  const float dd = qi < N ? Drow[(int64_t)bh * N + qi] : 0.f;
+
+  const uint32_t nbytes = (uint32_t)(((int64_t)(N - 1) * rs + D) * 2);
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(K + head_off), (short)0, nbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(V + head_off), (short)0, nbytes, 0x00020000);
+  const uint32_t row_bytes = (uint32_t)(rs * 2);
+  uint32_t voff_k[LOADS], voff_v[LOADS];
+  copy_offsets<D, LOADS, 1>(wave, lane, row_bytes, voff_k);
+  copy_offsets<D, LOADS, 0>(wave, lane, row_bytes, voff_v);
+  auto load_tile = [&](int stage, int k0) __attribute__((always_inline)) {
+    const uint32_t soff = (uint32_t)k0 * row_bytes;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      char* dst = smem + stage * G::STAGE + (wave * LOADS + i) * 1024;
+      copy_to_lds16(rk, dst, voff_k[i], soff);
+      copy_to_lds16(rv, dst + G::TILE, voff_v[i], soff);
+    }
+  };
+
+  // Row-read addresses: key row li, k-step t at (a0 ^ 32 t) (the swizzle XORs
+  // only chunk bits, so the k-step moves bits 5-7 of the address).
+  const uint32_t base = lds_addr(smem);
+  const uint32_t ka0 = base + li * G::RB + ((hh ^ G::swz_v(li)) * 16);
+  const uint32_t va0 = base + G::TILE + li * G::RB + ((hh ^ G::swz_k(li)) * 16);
+  uint32_t taddr[NE];
+  tr_addresses<D>(base, lane, taddr);
+
+  f32x16 dqacc[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) dqacc[e] = f32x16{};
+
+  auto tile = [&](auto st, auto masked, int k0) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st)::value;
+    constexpr bool MASKED = decltype(masked)::value != 0;
+    static_for<2>([&](auto JH) __attribute__((always_inline)) {
+      constexpr int jh = decltype(JH)::value;
+      bf16x8 f[NF];
+      static_for<NF>([&](auto T) __attribute__((always_inline)) {
+        constexpr int t = decltype(T)::value;
+        f[t] = read_b128<ST * G::STAGE + jh * 32 * G::RB>(ka0 ^ (uint32_t)(32 * t));
+      });
+      lds_wait_frags<NF>(f);
+      f32x16 sacc = {};
+#pragma unroll
+      for (int t = 0; t < NF; ++t) sacc = mfma_bf16(f[t], qf[t], sacc);
+      static_for<NF>([&](auto T) __attribute__((always_inline)) {
+        constexpr int t = decltype(T)::value;
+        f[t] = read_b128<ST * G::STAGE + jh * 32 * G::RB>(va0 ^ (uint32_t)(32 * t));
+      });
+      lds_wait_frags<NF>(f);
+      f32x16 dpacc = {};
+#pragma unroll
+      for (int t = 0; t < NF; ++t) dpacc = mfma_bf16(f[t], gf[t], dpacc);
+      bf16x8 ktf[2][NE];
+      read_tr_frags<D, ST * G::STAGE, jh>(taddr, ktf);
+      // P^T and dS^T; element v holds key k0 + 32 jh + 8 (v / 4) + 4 h + v % 4.
+      bf16x8 dsb[2];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float p = exp2_fast(__builtin_fmaf(sacc[v], scale_log2, -lse2));
+        if (MASKED) {
+          const int key = k0 + 32 * jh + 8 * (v >> 2) + 4 * hh + (v & 3);
+          if (key >= N || (CAUSAL && key > qi)) p = 0.f;
+        }
+        dsb[v >> 3][v & 7] = (__bf16)(p * (dpacc[v] - dd));
+      }
+      lds_wait_tr<NE>(ktf);
+#pragma unroll
+      for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int e = 0; e < NE; ++e) dqacc[e] = mfma_bf16(ktf[T][e], dsb[T], dqacc[e]);
+    });
+  };
+
+  const int nkb_all = ceil_div(N, kBC);
+  const int nkb = CAUSAL ? min(nkb_all, ceil_div(min(N, (qblk + 1) * kRowsB), kBC)) : nkb_all;
+  const int nkb_int = min(nkb, CAUSAL ? qblk * (kRowsB / kBC) : N / kBC) & ~1;
+#define STEP(ST_, KB, MASKED_)                                                                   \
+  do {                                                                                          \
+    const int kb_ = (KB);                                                                       \
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                           \
+    __syncthreads(); /* tile kb_ resident; every wave is done with the other stage */           \
+    if (kb_ + 1 < nkb) load_tile((ST_) ^ 1, (kb_ + 1) * kBC);                                   \
+    if (!(CAUSAL && kb_ * kBC > q0 + 31)) tile(IC<ST_>{}, IC<MASKED_>{}, kb_ * kBC);            \
+  } while (0)
+  load_tile(0, 0);
+  int kb = 0;
+  for (; kb < nkb_int; kb += 2) {
+    STEP(0, kb, 0);
+    STEP(1, kb + 1, 0);
+  }
+  for (; kb < nkb; kb += 2) {
+    STEP(0, kb, 1);
+    if (kb + 1 < nkb) STEP(1, kb + 1, 1);
+  }
+#undef STEP
+  if (qi < N) store_rows<D>(dQ + head_off + (int64_t)qi * rs, dqacc, scale, hh);
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV.  LDS: [2 stages x (LSE*log2e[64], D[64])] then 2 stages x (Q tile,
+// dO tile), both tiles swz_v (read row-wise and transposed).
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64 * kNWb, 1) void bwd_dkdv_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const __bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Drow,
+    __bf16* __restrict__ dK, __bf16* __restrict__ dV, int H, int N, float scale_log2, float scale,
+    int nkb, int xcd_remap) {
+  using G = Geo<D>;
+  constexpr int NF = D / 16, NE = D / 32;
+  constexpr int LOADS = G::TILE / (1024 * kNWb);
+  constexpr int ROWV = 1024;  // bytes of per-row vectors (2 stages x 2 x 64 floats)
+  __shared__ __attribute__((aligned(1024))) char smem[ROWV + 2 * G::STAGE];
+  char* tiles = smem + ROWV;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31, hh = lane >> 5;
+  int L = blockIdx.x;
+  if (xcd_remap) L = (L & 7) * (gridDim.x >> 3) + (L >> 3);
+  const int kblk = L % nkb, bh = L / nkb;  // causal: low key blocks see the most queries
+  const int b = bh / H, h = bh - b * H;
+  const int64_t rs = (int64_t)H * D;
+  const int64_t head_off = ((int64_t)b * N * H + h) * D;
+  const int k0w = kblk * kRowsB + wave * 32;  // this wave's first key
+  const int kj = k0w + li;                    // this lane's key (MFMA column)
+
+  // K^T and V^T as B operands: k-step t, half h -> dims 16 t + 8 h .. +7 of key kj.
+  bf16x8 kt[NF], vt[NF];
+#pragma unroll
+  for (int t = 0; t < NF; ++t) {
+    const bf16x8 z = {};
+    kt[t] = kj < N ? *(const bf16x8*)(K + head_off + (int64_t)kj * rs + 16 * t + 8 * hh) : z;
+    vt[t] = kj < N ? *(const bf16x8*)(V + head_off + (int64_t)kj * rs + 16 * t + 8 * hh) : z;
+  }
+
+  const uint32_t nbytes = (uint32_t)(((int64_t)(N - 1) * rs + D) * 2);
+  const __amdgpu_buffer_rsrc_t rq =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(Q + head_off), (short)0, nbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rg =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(dO + head_off), (short)0, nbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(L2 + (int64_t)bh * N), (short)0, (uint32_t)N * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(Drow + (int64_t)bh * N), (short)0, (uint32_t)N * 4, 0x00020000);
+  const uint32_t row_bytes = (uint32_t)(rs * 2);
+  uint32_t voff[LOADS];
+  copy_offsets<D, LOADS, 1>(wave, lane, row_bytes, voff);
+  auto load_tile = [&](int stage, int i0) __attribute__((always_inline)) {
+    const uint32_t soff = (uint32_t)i0 * row_bytes;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      char* dst = tiles + stage * G::STAGE + (wave * LOADS + i) * 1024;
+      copy_to_lds16(rq, dst, voff[i], soff);
+      copy_to_lds16(rg, dst + G::TILE, voff[i], soff);
+    }
+    // 64 floats of LSE*log2e (lanes 0-15) and of D (lanes 16-31), by wave 0;
+    // lane i's 16 bytes land at 16 i, so D follows LSE.
+    if (wave == 0 && lane < 32) {
+      char* dst = smem + stage * 512;
+      if (lane < 16)
+        copy_to_lds16(rl, dst, (uint32_t)lane * 16, (uint32_t)i0 * 4);
+      else
+        copy_to_lds16(rd, dst, (uint32_t)(lane - 16) * 16, (uint32_t)i0 * 4);
+    }
+  };
+
+  const uint32_t base = lds_addr(tiles);
+  const uint32_t qa0 = base + li * G::RB + ((hh ^ G::swz_v(li)) * 16);  // row li, k-step t at ^ 32 t
+  const uint32_t la0 = lds_addr(smem) + hh * 16;
+  uint32_t taddr[NE];
+  tr_addresses<D>(base, lane, taddr);
+
+  f32x16 dvacc[NE], dkacc[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) dvacc[e] = dkacc[e] = f32x16{};
+
+  auto tile = [&](auto st, auto masked, int i0) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st)::value;
+    constexpr bool MASKED = decltype(masked)::value != 0;
+    static_for<2>([&](auto JQ) __attribute__((always_inline)) {
+      constexpr int jq = decltype(JQ)::value;
+      const int iq0 = i0 + 32 * jq;
+      if (CAUSAL && iq0 + 31 < k0w) return;  // every query before every key of this wave
+      bf16x8 f[NF];
+      static_for<NF>([&](auto T) __attribute__((always_inline)) {
+        constexpr int t = decltype(T)::value;
+        f[t] = read_b128<ST * G::STAGE + jq * 32 * G::RB>(qa0 ^ (uint32_t)(32 * t));
+      });
+      lds_wait_frags<NF>(f);
+      f32x16 sacc = {};
+#pragma unroll
+      for (int t = 0; t < NF; ++t) sacc = mfma_bf16(f[t], kt[t], sacc);
+      static_for<NF>([&](auto T) __attribute__((always_inline)) {
+        constexpr int t = decltype(T)::value;
+        f[t] = read_b128<ST * G::STAGE + G::TILE + jq * 32 * G::RB>(qa0 ^ (uint32_t)(32 * t));
+      });
+      lds_wait_frags<NF>(f);
+      f32x16 dpacc = {};
+#pragma unroll
+      for (int t = 0; t < NF; ++t) dpacc = mfma_bf16(f[t], vt[t], dpacc);
+      // LSE*log2e and D of this lane's 16 query rows 32 jq + 8 g + 4 h + (0..3).
+      f32x4 l4[4], d4[4];
+      static_for<4>([&](auto Gi) __attribute__((always_inline)) {
+        constexpr int g = decltype(Gi)::value;
+        l4[g] = read_f4<ST * 512 + (32 * jq + 8 * g) * 4>(la0);
+        d4[g] = read_f4<ST * 512 + 256 + (32 * jq + 8 * g) * 4>(la0);
+      });
+      lds_wait_f4(l4, d4);
+      bf16x8 pb[2], dsb[2];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float p = exp2_fast(__builtin_fmaf(sacc[v], scale_log2, -l4[v >> 2][v & 3]));
+        if (MASKED) {
+          const int q = iq0 + 8 * (v >> 2) + 4 * hh + (v & 3);
+          if (q >= N || (CAUSAL && kj > q)) p = 0.f;
+        }
+        pb[v >> 3][v & 7] = (__bf16)p;
+        dsb[v >> 3][v & 7] = (__bf16)(p * (dpacc[v] - d4[v >> 2][v & 3]));
+      }
+      bf16x8 tf[2][NE];
+      read_tr_frags<D, ST * G::STAGE + G::TILE, jq>(taddr, tf);  // dO^T
+      lds_wait_tr<NE>(tf);
+#pragma unroll
+      for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int e = 0; e < NE; ++e) dvacc[e] = mfma_bf16(tf[T][e], pb[T], dvacc[e]);
+      read_tr_frags<D, ST * G::STAGE, jq>(taddr, tf);  // Q^T
+      lds_wait_tr<NE>(tf);
+#pragma unroll
+      for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int e = 0; e < NE; ++e) dkacc[e] = mfma_bf16(tf[T][e], dsb[T], dkacc[e]);
+    });
+  };
+
+  // Query tiles: causal starts at the tile holding the workgroup's first key.
+  const int nqt = ceil_div(N, kBC);
+  const int qt0 = CAUSAL ? (kblk * kRowsB) / kBC : 0;
+#define STEP(ST_, QT)                                                                            \
+  do {                                                                                          \
+    const int qt_ = (QT);                                                                       \
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                           \
+    __syncthreads(); /* tile qt_ resident; every wave is done with the other stage */           \
+    if (qt_ + 1 < nqt) load_tile((ST_) ^ 1, (qt_ + 1) * kBC);                                   \
+    const int i0_ = qt_ * kBC;                                                                  \
+    if (!(CAUSAL && i0_ + kBC - 1 < k0w)) {                                                     \
+      if (i0_ + kBC > N || (CAUSAL && i0_ < k0w + 31))                                          \
+        tile(IC<ST_>{}, IC<1>{}, i0_);                                                          \
+      else                                                                                      \
+        tile(IC<ST_>{}, IC<0>{}, i0_);                                                          \
+    }                                                                                           \
+  } while (0)
+  load_tile(0, qt0 * kBC);
+  int qt = qt0;
+  for (; qt + 1 < nqt; qt += 2) {
+    STEP(0, qt);
+    STEP(1, qt + 1);
+  }
+  if (qt < nqt) STEP(0, qt);
+#undef STEP
+  if (kj < N) {
+    store_rows<D>(dK + head_off + (int64_t)kj * rs, dkacc, scale, hh);
+    store_rows<D>(dV + head_off + (int64_t)kj * rs, dvacc, 1.f, hh);
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv, float* ws, int B, int H,
+                      int N, float scale, hipStream_t stream) {
+  const int64_t rows = (int64_t)B * N * H;
+  float* drow = ws;
+  float* l2 = ws + rows;
+  constexpr int RPB = 256 / (D / 8);  // rows per prep block
+  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
+                     stream, (const __bf16*)o, (const __bf16*)dout, lse, drow, l2, H, N, rows);
+  const int nb = (N + kRowsB - 1) / kRowsB;
+  const int64_t grid = (int64_t)B * H * nb;
+  const int remap = (grid % 8 == 0) ? 1 : 0;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(64 * kNWb), 0, stream,
+                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, l2,
+                     drow, (__bf16*)dk, (__bf16*)dv, H, N, scale * kLog2e, scale, nb, remap);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(64 * kNWb), 0, stream,
+                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, l2,
+                     drow, (__bf16*)dq, H, N, scale * kLog2e, scale, nb, remap);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                                const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                float* workspace, int B, int H, int N, int d, bool causal,
+                                float softmax_scale, hipStream_t stream) {
+  if (d == 128)
+    return causal ? launch_bwd<128, true>(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N,
+                                          softmax_scale, stream)
+                  : launch_bwd<128, false>(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N,
+                                           softmax_scale, stream);
+  return causal ? launch_bwd<64, true>(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N,
+                                       softmax_scale, stream)
+                : launch_bwd<64, false>(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N,
+                                        softmax_scale, stream);
+}
+
+}  // namespace exattn

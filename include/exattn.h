@@ -110,6 +110,29 @@ int attn_fwd_fp8_gqa(const void* q8, const void* k8, const void* v8,
                      void* stream);
 
 /*
+ * Gradients of attn_fwd_bf16 (FlashAttention-3 report, section 3.4: FA-2's
+ * recompute strategy, P rebuilt from Q, K and the saved log-sum-exp).
+ *   q, k, v      the forward's bfloat16 BSHD inputs.
+ *   o, lse       the forward's outputs (bf16 BSHD O and fp32 [B, H, N] LSE,
+ *                natural log, as attn_fwd_bf16 writes them).
+ *   dout         bfloat16 BSHD gradient of the loss with respect to O.
+ *   dq, dk, dv   bfloat16 BSHD outputs: the gradients with respect to q, k, v.
+ *   workspace    device memory of attn_bwd_bf16_workspace_bytes(B, H, N) bytes
+ *                (fp32, 4-byte aligned), owned by the caller; its contents on
+ *                entry do not matter and are overwritten.
+ *   causal, softmax_scale   as in the forward call that produced o and lse.
+ * With P = exp(scale Q K^T - LSE) and D_i = sum_c dO[i,c] O[i,c] per row:
+ * dV = P^T dO, dS = P * (dO V^T - D), dQ = scale dS K, dK = scale dS^T Q.
+ * P and dS are rounded to bf16 for the matrix products, which accumulate in
+ * fp32.  Outputs must not overlap any input, each other or the workspace
+ * (EXATTN_ERR_VALUE).  Three kernels are launched on `stream`.
+ */
+long long attn_bwd_bf16_workspace_bytes(int B, int H, int N);
+int attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv, float* workspace,
+                  int B, int H, int N, int d, int causal, float softmax_scale, void* stream);
+
+/*
  * FP8 pre-pass: optional incoherent rotation, then block quantisation to e4m3
  * (FlashAttention-3 report, sections 2.2 and 3.3).
  *   x        bfloat16 BSHD input.

@@ -20,7 +20,8 @@ P2 = 2 << 30
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:long\s+)?\w+\s*\*?\s*(\w+)\s*\(", text,
+                                 flags=re.M)))
 
 
 def _codes():
@@ -30,12 +31,13 @@ def _codes():
 
 def test_library_builds_and_loads():
     assert os.path.exists(ea.LIB_PATH)
-    assert ea.lib().exattn_abi_version() == 2
+    assert ea.lib().exattn_abi_version() == 3
 
 
 def test_exports_every_declared_symbol():
     names = _declared()
     assert set(names) == {"attn_fwd_bf16", "attn_fwd_fp8", "attn_fwd_bf16_gqa", "attn_fwd_fp8_gqa",
+                          "attn_bwd_bf16", "attn_bwd_bf16_workspace_bytes",
                           "blockquant_hadamard", "exattn_strerror", "exattn_abi_version"}
     raw = ctypes.CDLL(ea.LIB_PATH)
     for n in names:
@@ -140,3 +142,28 @@ def test_blockquant_validation():
     assert _bq(signs=P + 3 * P2 + 2) == ea.ERR_ALIGN
     assert _bq(x8=P + 100 * 16) == ea.ERR_VALUE  # output inside the input
     assert _bq(N=0) == 0
+
+
+def _bwd(q=P, k=P + P2, v=P + 2 * P2, o=P + 3 * P2, do=P + 4 * P2, lse=P + 5 * P2, dq=P + 6 * P2,
+         dk=P + 7 * P2, dv=P + 8 * P2, ws=P + 9 * P2, B=1, H=2, N=256, d=64, causal=0, scale=0.125):
+    return ea.lib().attn_bwd_bf16(q, k, v, o, do, lse, dq, dk, dv, ws, B, H, N, d, causal, scale,
+                                  None)
+
+
+def test_bwd_validation():
+    assert ea.lib().attn_bwd_bf16_workspace_bytes(2, 3, 100) == 8 * 2 * 3 * 100
+    assert ea.lib().attn_bwd_bf16_workspace_bytes(-1, 3, 100) == ea.ERR_SHAPE
+    for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "ws"):
+        assert _bwd(**{name: None}) == ea.ERR_NULL, name
+    assert _bwd(d=96) == ea.ERR_SHAPE
+    assert _bwd(N=-1) == ea.ERR_SHAPE
+    assert _bwd(scale=0.0) == ea.ERR_VALUE
+    assert _bwd(causal=3) == ea.ERR_VALUE
+    assert _bwd(dq=P + 6 * P2 + 8) == ea.ERR_ALIGN
+    assert _bwd(ws=P + 9 * P2 + 2) == ea.ERR_ALIGN
+    assert _bwd(dq=P + 64) == ea.ERR_VALUE            # dQ overlaps q
+    assert _bwd(dk=P + 6 * P2 + 64) == ea.ERR_VALUE   # dK overlaps dQ
+    assert _bwd(ws=P + 8 * P2 + 64) == ea.ERR_VALUE   # workspace overlaps dV
+    assert _bwd(ws=P + 5 * P2) == ea.ERR_VALUE        # workspace overlaps the LSE
+    assert _bwd(B=0) == 0
+    assert _bwd(N=0, q=None) == 0
