@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--B8", type=int, default=4, help="batch of the fp8 leg")
     p.add_argument("--H", type=int, default=16)
     p.add_argument("--d", type=int, default=128)
+    p.add_argument("--bwd-reps", type=int, default=20,
+                   help="timed launches of the bf16 gradients (attn_bwd_bf16) on the bf16 "
+                        "workload, after the timed steps; 0 skips them")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run one plain 256 MiB device copy (untimed), the reference that "
                         "scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -238,6 +241,38 @@ def main():
                      "algorithmic_flops_per_launch": w16.flops()},
         "outputs_finite": ok,
     }
+    if a.bwd_reps > 0:
+        # Gradients of the bf16 forward (not part of the forward step above):
+        # dO seeded N(0,1), O and LSE from the last timed step.
+        print(f"[bench] backward: {a.bwd_reps} launches", file=sys.stderr, flush=True)
+        do = dev_bf16(workloads.gen_random((B, N, H, d), 1002))
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        ws = torch.empty(max(1, ea.lib().attn_bwd_bf16_workspace_bytes(B, H, N) // 4),
+                         dtype=torch.float32, device=dev)
+
+        def bwd():
+            ea.attn_bwd_bf16(q, k, v, o16, lse16, do, causal=a.causal, softmax_scale=scale,
+                             dq=dq, dk=dk, dv=dv, workspace=ws)
+        for _ in range(3):
+            bwd()
+        bev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+               for _ in range(a.bwd_reps)]
+        for e0, e1 in bev:
+            e0.record(stream)
+            bwd()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        tb = [e0.elapsed_time(e1) for e0, e1 in bev]
+        t_bwd = float(np.median(tb)) * 1e-3
+        bflops = 2.5 * w16.flops()  # five N^2 d products against the forward's two
+        out["backward"] = {
+            "kernel": "attn_bwd_bf16 (prep + dK/dV + dQ kernels)", "workload": w16.name,
+            "value": round(bflops / t_bwd / 1e12, 2), "unit": "TFLOP/s",
+            "flops_counted": "2.5 x forward (10 B H N^2 d, halved for causal)",
+            "pct_of_peak": round(100 * bflops / t_bwd / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "ms": round(t_bwd * 1e3, 4), "reps": a.bwd_reps,
+            "timing": "median of per-call HIP event times",
+            "finite": bool(all(torch.isfinite(x).all().item() for x in (dq, dk, dv)))}
     if not a.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w16, a.cpu_seconds)
