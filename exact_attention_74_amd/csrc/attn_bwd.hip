@@ -30,8 +30,8 @@
 // LDS tiles are 64 rows, copied by buffer_load ... lds (reads past the end of
 // the sequence return zeros) and double-buffered, as in the forward.  A tile
 // that is read both row-wise (ds_read_b128, an A operand) and transposed
-// (ds_read_b64_tr_b16) uses the chunk swizzle of the transposed reads, which
-// keeps the immediate offsets of both read patterns valid.
+// (ds_read_b64_tr_b16) uses the chunk swizzle swz_b, free of bank conflicts
+// for both patterns.
 #include "common.h"
 #include "launch.h"
 #include "lds_tile.h"
@@ -71,9 +71,10 @@ __device__ __forceinline__ f32x4 read_f4(uint32_t addr) {
 }
 
 // Transposed-read A-operand fragments for the 32 rows [32 J, 32 J + 32) of the
-// tile at LDS offset OFF: frag[T][e] covers rows 32 J + 16 T .. +15 (k) and
-// d-rows 32 e .. 32 e + 31, in the accumulator's row order (row 16 T +
-// 8 (s / 4) + 4 h + s % 4 in k-slot s of half-wave h).
+// tile at LDS offset OFF (swizzle swz_b): frag[T][e] covers rows 32 J + 16 T ..
+// +15 (k) and d-rows 32 e .. 32 e + 31, in the accumulator's row order (row
+// 16 T + 8 (s / 4) + 4 h + s % 4 in k-slot s of half-wave h).  Rows + 8 and
+// + 24 sit at the address XOR 32 (swz_b(row + 8) = swz_b(row) ^ 2).
 template <int D, int OFF, int J>
 __device__ __forceinline__ void read_tr_frags(const uint32_t (&taddr)[D / 32],
                                               bf16x8 (&frag)[2][D / 32]) {
@@ -85,8 +86,8 @@ __device__ __forceinline__ void read_tr_frags(const uint32_t (&taddr)[D / 32],
       constexpr int R0 = 32 * J;
       const bf16x4 lo = T == 0 ? read_tr16<OFF + (R0 + 0) * G::RB>(taddr[e])
                                : read_tr16<OFF + (R0 + 16) * G::RB>(taddr[e]);
-      const bf16x4 hi = T == 0 ? read_tr16<OFF + (R0 + 8) * G::RB>(taddr[e])
-                               : read_tr16<OFF + (R0 + 24) * G::RB>(taddr[e]);
+      const bf16x4 hi = T == 0 ? read_tr16<OFF + (R0 + 8) * G::RB>(taddr[e] ^ 32u)
+                               : read_tr16<OFF + (R0 + 24) * G::RB>(taddr[e] ^ 32u);
       frag[T][e] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   }
@@ -104,7 +105,7 @@ __device__ __forceinline__ void lds_wait_tr(bf16x8 (&f)[2][NE]) {
 }
 
 // LDS address of this lane's transposed-read source in a tile at LDS byte
-// address `base` (rows key-major, chunk swizzle swz_v): row 4 hv + j, chunk
+// address `base` (rows key-major, chunk swizzle swz_b): row 4 hv + j, chunk
 // 4 e + 2 (g % 2) + q / 2, half q % 2.
 template <int D>
 __device__ __forceinline__ void tr_addresses(uint32_t base, int lane, uint32_t (&taddr)[D / 32]) {
@@ -115,12 +116,12 @@ __device__ __forceinline__ void tr_addresses(uint32_t base, int lane, uint32_t (
 #pragma unroll
   for (int e = 0; e < D / 32; ++e) {
     const int c = 4 * e + 2 * (g & 1) + (q >> 1);
-    taddr[e] = base + row * G::RB + ((c ^ G::swz_v(row)) * 16) + (q & 1) * 8;
+    taddr[e] = base + row * G::RB + ((c ^ G::swz_b(row)) * 16) + (q & 1) * 8;
   }
 }
 
 // Global -> LDS copy offsets of this lane's chunks of a 64-row tile, for a
-// layout with chunk swizzle SWZ (0: swz_k, 1: swz_v).
+// layout with chunk swizzle SWZ (0: swz_k, 1: swz_b).
 template <int D, int LOADS, int SWZ>
 __device__ __forceinline__ void copy_offsets(int wave, int lane, uint32_t row_bytes,
                                              uint32_t (&voff)[LOADS]) {
@@ -129,7 +130,7 @@ __device__ __forceinline__ void copy_offsets(int wave, int lane, uint32_t row_by
   for (int i = 0; i < LOADS; ++i) {
     const int chunk = (wave * LOADS + i) * 64 + lane;
     const int row = chunk / G::CPR, pos = chunk % G::CPR;
-    const int sw = SWZ ? G::swz_v(row) : G::swz_k(row);
+    const int sw = SWZ ? G::swz_b(row) : G::swz_k(row);
     voff[i] = row * row_bytes + (uint32_t)((pos ^ sw) * 16);
   }
 }
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// dQ: the forward kernel's layout.  Stage: K tile (swz_v: read as the S^T A
+// dQ: the forward kernel's layout.  Stage: K tile (swz_b: read as the S^T A
 // operand and transposed for K^T), V tile (swz_k: read as the dP^T A operand).
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * kNWb, 2) void bwd_dq_kernel(
@@ -240,7 +241,7 @@ __global__ __launch_bounds__(64 * kNWb, 2) void bwd_dq_kernel(
   // Row-read addresses: key row li, k-step t at (a0 ^ 32 t) (the swizzle XORs
   // only chunk bits, so the k-step moves bits 5-7 of the address).
   const uint32_t base = lds_addr(smem);
-  const uint32_t ka0 = base + li * G::RB + ((hh ^ G::swz_v(li)) * 16);
+  const uint32_t ka0 = base + li * G::RB + ((hh ^ G::swz_b(li)) * 16);
   const uint32_t va0 = base + G::TILE + li * G::RB + ((hh ^ G::swz_k(li)) * 16);
   uint32_t taddr[NE];
   tr_addresses<D>(base, lane, taddr);
@@ -319,7 +320,7 @@ __global__ __launch_bounds__(64 * kNWb, 2) void bwd_dq_kernel(
 
 // ---------------------------------------------------------------------------
 // dK, dV.  LDS: [2 stages x (LSE*log2e[64], D[64])] then 2 stages x (Q tile,
-// dO tile), both tiles swz_v (read row-wise and transposed).
+// dO tile), both tiles swz_b (read row-wise and transposed).
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * kNWb, 1) void bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
@@ -386,7 +387,7 @@ __global__ __launch_bounds__(64 * kNWb, 1) void bwd_dkdv_kernel(
   };
 
   const uint32_t base = lds_addr(tiles);
-  const uint32_t qa0 = base + li * G::RB + ((hh ^ G::swz_v(li)) * 16);  // row li, k-step t at ^ 32 t
+  const uint32_t qa0 = base + li * G::RB + ((hh ^ G::swz_b(li)) * 16);  // row li, k-step t at ^ 32 t
   const uint32_t la0 = lds_addr(smem) + hh * 16;
   uint32_t taddr[NE];
   tr_addresses<D>(base, lane, taddr);

@@ -26,6 +26,14 @@ struct Geo {
   // chunk position of chunk c of row `row`
   __device__ static int swz_k(int row) { return (row / RP) % CPR; }
   __device__ static int swz_v(int row) { return 4 * ((row / RP) % (CPR / 4)); }
+  // For a tile read both ways (ds_read_b128 rows and ds_read_b64_tr_b16):
+  // swz_v plus (row / 4) % 4 in the low chunk bits.  16 consecutive rows get
+  // 16 distinct chunk positions (row reads without bank conflicts), rows 0-3
+  // keep swz_v's separation (transposed reads without conflicts), and
+  // swz_b(row + 16) = swz_b(row), swz_b(row + 8) = swz_b(row) ^ 2, so the
+  // transposed reads of rows + 8 use the address XOR 32 with the same
+  // immediate offsets.
+  __device__ static int swz_b(int row) { return swz_v(row) + (row / 4) % 4; }
 };
 
 // Asynchronous 16-byte-per-lane copy global -> LDS; lane i's chunk lands at
