@@ -15,12 +15,15 @@ Modules:
                 K/V head mapping) and the tiled online-softmax recurrence,
                 both in fp64.
   backward   -- the gradients dQ, dK, dV of exact attention (the definition).
+  rope       -- rotary position embedding (fp64 definition, fp32 emulation),
+                applied before the FP8 pre-pass in the fused form.
   fp8        -- OCP e4m3 encode/decode, fast Walsh-Hadamard transform, the
                 block-quantise + incoherent-processing pre-pass, and the FP8
                 attention emulation.
 """
 from .attention import kv_head, naive_attention, naive_attention_rows, tiled_attention  # noqa: F401
 from .backward import attention_backward, attention_backward_heads  # noqa: F401
+from .rope import rope_fp32, rope_fp64  # noqa: F401
 from .fp8 import (  # noqa: F401
     E4M3_MAX, e4m3_decode_table, e4m3_encode, e4m3_decode, fwht, sylvester_hadamard,
     rotate_fp64, blockquant_hadamard, dequantize, fp8_attention_emulation,

@@ -115,6 +115,15 @@ def gen_qkv_gqa(B: int, N: int, H: int, Hkv: int, d: int, seed: int, dist: str =
     return q, k, v
 
 
+def rope_tables(N: int, d: int, base: float = 10000.0, offset: int = 0):
+    """cos, sin tables [N, d/2] (float32) of the usual RoPE frequency schedule,
+    angle (offset + n) * base^(-2 i / d), evaluated in fp64 and rounded once."""
+    n = np.arange(N, dtype=np.float64)[:, None] + offset
+    inv = base ** (-2.0 * np.arange(d // 2, dtype=np.float64) / d)
+    ang = n * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
 def gen_signs(d: int, seed: int = SIGNS_SEED) -> np.ndarray:
     """d random signs (+1/-1, float32) for the incoherent-processing diagonal."""
     rng = np.random.default_rng(seed)
