@@ -13,6 +13,7 @@ Entry points (same names as the C ABI):
   attn_fwd_bf16_gqa / attn_fwd_fp8_gqa: the same with K/V (and their scales) on
     H_kv heads, H a multiple of H_kv (grouped-query / multi-query attention).
   attn_bwd_bf16(q, k, v, o, lse, do, causal=False, softmax_scale=None) -> (dq, dk, dv)
+  rope_blockquant_hadamard(x, cos, sin, interleaved, signs=None, block_rows=128) -> (x8, scale)
 Tensors are BSHD (batch, seqlen, heads, head_dim), contiguous, on a HIP device.
 """
 from __future__ import annotations
@@ -37,6 +38,7 @@ SIGNATURES = {
     "attn_fwd_fp8_gqa": [_c_void_p] * 8 + [_c_int] * 6 + [_c_float, _c_void_p],
     "attn_bwd_bf16": [_c_void_p] * 10 + [_c_int] * 5 + [_c_float, _c_void_p],
     "attn_bwd_bf16_workspace_bytes": [_c_int] * 3,
+    "rope_blockquant_hadamard": [_c_void_p] * 6 + [_c_int] * 6 + [_c_void_p],
     "blockquant_hadamard": [_c_void_p] * 4 + [_c_int] * 5 + [_c_void_p],
     "exattn_strerror": [_c_int],
     "exattn_abi_version": [],
@@ -183,6 +185,30 @@ def _fp8(fn, q8, k8, v8, q_scale, k_scale, v_scale, causal, softmax_scale, out, 
     return out, lse
 
 
+def rope_blockquant_hadamard(x, cos, sin, interleaved: bool, signs: torch.Tensor | None = None,
+                             block_rows: int = 128, out: torch.Tensor | None = None,
+                             scale: torch.Tensor | None = None):
+    """blockquant_hadamard of x after a rotary embedding with the float32
+    cos/sin tables [N, d/2] (pairs (2i, 2i+1) if ``interleaved`` else (i, i+d/2))."""
+    B, N, H, d = _check_bshd("x", x, torch.bfloat16)
+    for name, t in (("cos", cos), ("sin", sin)):
+        if (not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.device != x.device
+                or tuple(t.shape) != (N, d // 2) or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 [N, d/2] tensor on x's device")
+    if signs is not None:
+        if signs.device != x.device or signs.dtype != torch.float32 or signs.numel() != d:
+            raise ValueError("signs must be d float32 values on the same device")
+        signs = signs.contiguous()
+    if out is None:
+        out = torch.empty((B, N, H, d), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty((B, H, (N + 127) // 128), dtype=torch.float32, device=x.device)
+    _call("rope_blockquant_hadamard", x.data_ptr(), out.data_ptr(), scale.data_ptr(),
+          signs.data_ptr() if signs is not None else None, cos.data_ptr(), sin.data_ptr(),
+          int(bool(interleaved)), B, H, N, d, int(block_rows), _stream_ptr(x))
+    return out, scale
+
+
 def attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False,
                  softmax_scale: float | None = None, out: torch.Tensor | None = None,
                  lse: torch.Tensor | None = None):
@@ -235,5 +261,5 @@ def attn_bwd_bf16(q, k, v, o, lse, do, causal: bool = False, softmax_scale: floa
 
 
 __all__ = ["attn_fwd_bf16", "attn_fwd_fp8", "attn_fwd_bf16_gqa", "attn_fwd_fp8_gqa", "attn_bwd_bf16",
-           "blockquant_hadamard", "lib", "strerror",
+           "blockquant_hadamard", "rope_blockquant_hadamard", "lib", "strerror",
            "ExattnError", "LIB_PATH", "SIGNATURES"]

@@ -43,7 +43,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? EXATTN_OK : EXATTN_ERR_H
 
 extern "C" {
 
-int exattn_abi_version(void) { return 3; }
+int exattn_abi_version(void) { return 4; }
 
 const char* exattn_strerror(int code) {
   switch (code) {
@@ -170,6 +170,25 @@ int blockquant_hadamard(const void* x, void* x8, float* scale, const float* sign
   if (overlap(x8, n, x, 2 * n)) return EXATTN_ERR_VALUE;
   return hip_status(
       exattn::launch_blockquant(x, x8, scale, signs, B, H, N, d, block_rows, (hipStream_t)stream));
+}
+
+int rope_blockquant_hadamard(const void* x, void* x8, float* scale, const float* signs,
+                             const float* rope_cos, const float* rope_sin, int rope_interleaved,
+                             int B, int H, int N, int d, int block_rows, void* stream) {
+  int rc = check_shape(B, H, N, d, 2);
+  if (rc) return rc;
+  if (block_rows != 0 && block_rows != 128) return EXATTN_ERR_VALUE;
+  if (rope_interleaved != 0 && rope_interleaved != 1) return EXATTN_ERR_VALUE;
+  const int64_t n = (int64_t)B * N * H * d;
+  if (n == 0) return EXATTN_OK;
+  if (!x || !x8 || !scale || !rope_cos || !rope_sin) return EXATTN_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(x8, 16) || !aligned(scale, 4) || (signs && !aligned(signs, 4)) ||
+      !aligned(rope_cos, 16) || !aligned(rope_sin, 16))
+    return EXATTN_ERR_ALIGN;
+  if (overlap(x8, n, x, 2 * n)) return EXATTN_ERR_VALUE;
+  return hip_status(exattn::launch_rope_blockquant(x, x8, scale, signs, rope_cos, rope_sin,
+                                                   rope_interleaved != 0, B, H, N, d, block_rows,
+                                                   (hipStream_t)stream));
 }
 
 }  // extern "C"

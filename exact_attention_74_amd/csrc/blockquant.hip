@@ -12,6 +12,14 @@
 // increasing-stride order.  The block's amax is
 // reduced across the workgroup, then the codes are
 // e4m3_rne(y * fp32(448 / amax)).
+//
+// Fused rotary embedding (FlashAttention-3 report, sections 2.2 and 3.3: the
+// quantisation can ride on the memory-bound RoPE pass).  With ROPE != 0 each
+// row n is first rotated by the caller's cos/sin tables [N, d/2]: pair
+// (a, b) -> (a cos - b sin, a sin + b cos), pairs (2i, 2i+1) (ROPE = 1,
+// interleaved) or (i, i + d/2) (ROPE = 2, half-split).  Both pairings fall
+// inside one lane's chunks; products and sums are rounded separately (no
+// fused multiply-add), the fp32 arithmetic the test oracle emulates.
 #include "common.h"
 #include "launch.h"
 
@@ -32,11 +40,24 @@ __device__ __forceinline__ float quad_xor(float v) {
                                                             0xF, true));
 }
 
-template <int D, bool ROTATE, int MODE>
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// One RoPE pair: (a, b) -> (a c - b s, a s + b c), each product and the sum /
+// difference rounded to fp32 on its own (contraction into fma switched off).
+__device__ __forceinline__ void rope_pair(float& a, float& b, float c, float s) {
+#pragma clang fp contract(off)
+  const float ac = a * c, bs = b * s, as = a * s, bc = b * c;
+  a = ac - bs;
+  b = as + bc;
+}
+
+template <int D, bool ROTATE, int MODE, int ROPE>
 __global__ __launch_bounds__(kThreads) void blockquant_kernel(const __bf16* __restrict__ X,
                                                               uint8_t* __restrict__ X8,
                                                               float* __restrict__ S,
                                                               const float* __restrict__ signs,
+                                                              const float* __restrict__ rcos,
+                                                              const float* __restrict__ rsin,
                                                               int H, int N, int nsb, float kconst) {
   constexpr int LPR = 4;                 // lanes per row
   constexpr int EPL = D / LPR;           // elements per lane (32 or 16)
@@ -69,6 +90,42 @@ __global__ __launch_bounds__(kThreads) void blockquant_kernel(const __bf16* __re
       if (row < N) xv = *(const bf16x8*)(X + head_off + (int64_t)row * rs + 32 * c + 8 * lr);
 #pragma unroll
       for (int k = 0; k < 8; ++k) y[p][c][k] = (float)xv[k];
+    }
+  }
+  if constexpr (ROPE != 0) {
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int row = sb * kRows + p * RPP + rsub;
+      if (row < N) {
+        const float* cr = rcos + (int64_t)row * (D / 2);
+        const float* sr = rsin + (int64_t)row * (D / 2);
+        if constexpr (ROPE == 1) {
+          // element 32c + 8lr + k, k even, pairs with k + 1: pair 16c + 4lr + k/2
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            const f32x4 cv = *(const f32x4*)(cr + 16 * c + 4 * lr);
+            const f32x4 sv = *(const f32x4*)(sr + 16 * c + 4 * lr);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              rope_pair(y[p][c][2 * q], y[p][c][2 * q + 1], cv[q], sv[q]);
+            }
+          }
+        } else {
+          // element 32c + 8lr + k (c < NC/2) pairs with the same k of chunk c + NC/2
+#pragma unroll
+          for (int c = 0; c < NC / 2; ++c) {
+            const f32x4 c0 = *(const f32x4*)(cr + 32 * c + 8 * lr);
+            const f32x4 c1 = *(const f32x4*)(cr + 32 * c + 8 * lr + 4);
+            const f32x4 s0 = *(const f32x4*)(sr + 32 * c + 8 * lr);
+            const f32x4 s1 = *(const f32x4*)(sr + 32 * c + 8 * lr + 4);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              const float cs = k < 4 ? c0[k & 3] : c1[k & 3], sn = k < 4 ? s0[k & 3] : s1[k & 3];
+              rope_pair(y[p][c][k], y[p][c + NC / 2][k], cs, sn);
+            }
+          }
+        }
+      }
     }
   }
   float amax = 0.f;
@@ -185,9 +242,9 @@ __global__ __launch_bounds__(1024) void max_broadcast_kernel(float* __restrict__
   for (int i = threadIdx.x; i < n; i += 1024) S[i] = mx;
 }
 
-template <int D, bool ROTATE>
-hipError_t launch(const void* x, void* x8, float* scale, const float* signs, int B, int H, int N,
-                  int block_rows, hipStream_t stream) {
+template <int D, bool ROTATE, int ROPE>
+hipError_t launch(const void* x, void* x8, float* scale, const float* signs, const float* rcos,
+                  const float* rsin, int B, int H, int N, int block_rows, hipStream_t stream) {
   const int nsb = (N + kRows - 1) / kRows;
   const int64_t nslots = (int64_t)B * H * nsb;
   const unsigned grid = (unsigned)nslots;
@@ -195,32 +252,50 @@ hipError_t launch(const void* x, void* x8, float* scale, const float* signs, int
   const __bf16* xp = (const __bf16*)x;
   uint8_t* qp = (uint8_t*)x8;
   if (block_rows != 0) {
-    hipLaunchKernelGGL((blockquant_kernel<D, ROTATE, kQuantBlock>), dim3(grid), dim3(kThreads), 0,
-                       stream, xp, qp, scale, signs, H, N, nsb, kconst);
+    hipLaunchKernelGGL((blockquant_kernel<D, ROTATE, kQuantBlock, ROPE>), dim3(grid),
+                       dim3(kThreads), 0, stream, xp, qp, scale, signs, rcos, rsin, H, N, nsb, kconst);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((blockquant_kernel<D, ROTATE, kAmaxOnly>), dim3(grid), dim3(kThreads), 0,
-                     stream, xp, qp, scale, signs, H, N, nsb, kconst);
+  hipLaunchKernelGGL((blockquant_kernel<D, ROTATE, kAmaxOnly, ROPE>), dim3(grid), dim3(kThreads),
+                     0, stream, xp, qp, scale, signs, rcos, rsin, H, N, nsb, kconst);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(max_broadcast_kernel, dim3(1), dim3(1024), 0, stream, scale, (int)nslots);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((blockquant_kernel<D, ROTATE, kQuantGiven>), dim3(grid), dim3(kThreads), 0,
-                     stream, xp, qp, scale, signs, H, N, nsb, kconst);
+  hipLaunchKernelGGL((blockquant_kernel<D, ROTATE, kQuantGiven, ROPE>), dim3(grid),
+                     dim3(kThreads), 0, stream, xp, qp, scale, signs, rcos, rsin, H, N, nsb, kconst);
   return hipGetLastError();
+}
+
+template <int ROPE>
+hipError_t dispatch(const void* x, void* x8, float* scale, const float* signs, const float* rcos,
+                    const float* rsin, int B, int H, int N, int d, int block_rows,
+                    hipStream_t stream) {
+  const bool rot = signs != nullptr;
+  if (d == 128)
+    return rot ? launch<128, true, ROPE>(x, x8, scale, signs, rcos, rsin, B, H, N, block_rows,
+                                         stream)
+               : launch<128, false, ROPE>(x, x8, scale, signs, rcos, rsin, B, H, N, block_rows,
+                                          stream);
+  return rot ? launch<64, true, ROPE>(x, x8, scale, signs, rcos, rsin, B, H, N, block_rows, stream)
+             : launch<64, false, ROPE>(x, x8, scale, signs, rcos, rsin, B, H, N, block_rows,
+                                       stream);
 }
 
 }  // namespace
 
 hipError_t launch_blockquant(const void* x, void* x8, float* scale, const float* signs, int B, int H,
                              int N, int d, int block_rows, hipStream_t stream) {
-  const bool rot = signs != nullptr;
-  if (d == 128)
-    return rot ? launch<128, true>(x, x8, scale, signs, B, H, N, block_rows, stream)
-               : launch<128, false>(x, x8, scale, signs, B, H, N, block_rows, stream);
-  return rot ? launch<64, true>(x, x8, scale, signs, B, H, N, block_rows, stream)
-             : launch<64, false>(x, x8, scale, signs, B, H, N, block_rows, stream);
+  return dispatch<0>(x, x8, scale, signs, nullptr, nullptr, B, H, N, d, block_rows, stream);
+}
+
+hipError_t launch_rope_blockquant(const void* x, void* x8, float* scale, const float* signs,
+                                  const float* rcos, const float* rsin, bool interleaved, int B,
+                                  int H, int N, int d, int block_rows, hipStream_t stream) {
+  return interleaved
+             ? dispatch<1>(x, x8, scale, signs, rcos, rsin, B, H, N, d, block_rows, stream)
+             : dispatch<2>(x, x8, scale, signs, rcos, rsin, B, H, N, d, block_rows, stream);
 }
 
 }  // namespace exattn

@@ -26,4 +26,10 @@ hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
 hipError_t launch_blockquant(const void* x, void* x8, float* scale, const float* signs, int B, int H,
                              int N, int d, int block_rows, hipStream_t stream);
 
+// blockquant with a rotary embedding first: cos/sin tables [N, d/2] fp32,
+// pairs (2i, 2i+1) when interleaved, else (i, i + d/2).
+hipError_t launch_rope_blockquant(const void* x, void* x8, float* scale, const float* signs,
+                                  const float* rcos, const float* rsin, bool interleaved, int B,
+                                  int H, int N, int d, int block_rows, hipStream_t stream);
+
 }  // namespace exattn

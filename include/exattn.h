@@ -155,6 +155,22 @@ int attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, co
 int blockquant_hadamard(const void* x, void* x8, float* scale, const float* signs,
                         int B, int H, int N, int d, int block_rows, void* stream);
 
+/*
+ * The FP8 pre-pass fused with a rotary position embedding (FlashAttention-3
+ * report, sections 2.2 and 3.3: quantisation riding on the memory-bound RoPE
+ * pass, for Q and K).  As blockquant_hadamard, with each row n of x first
+ * rotated pairwise:
+ *   (x_a, x_b) -> (x_a cos[n][i] - x_b sin[n][i], x_a sin[n][i] + x_b cos[n][i])
+ *   rope_interleaved = 1: pairs (a, b) = (2i, 2i+1);  0: (i, i + d/2).
+ *   rope_cos, rope_sin   fp32 [N, d/2] device tables (16-byte aligned), the
+ *                caller's frequency schedule and position offset.
+ * The rotation is fp32 with every product and sum rounded separately; the
+ * quantised values are those of the rotated rows.
+ */
+int rope_blockquant_hadamard(const void* x, void* x8, float* scale, const float* signs,
+                             const float* rope_cos, const float* rope_sin, int rope_interleaved,
+                             int B, int H, int N, int d, int block_rows, void* stream);
+
 /* Static, never-NULL description of a return code. */
 const char* exattn_strerror(int code);
 

@@ -31,13 +31,13 @@ def _codes():
 
 def test_library_builds_and_loads():
     assert os.path.exists(ea.LIB_PATH)
-    assert ea.lib().exattn_abi_version() == 3
+    assert ea.lib().exattn_abi_version() == 4
 
 
 def test_exports_every_declared_symbol():
     names = _declared()
     assert set(names) == {"attn_fwd_bf16", "attn_fwd_fp8", "attn_fwd_bf16_gqa", "attn_fwd_fp8_gqa",
-                          "attn_bwd_bf16", "attn_bwd_bf16_workspace_bytes",
+                          "attn_bwd_bf16", "attn_bwd_bf16_workspace_bytes", "rope_blockquant_hadamard",
                           "blockquant_hadamard", "exattn_strerror", "exattn_abi_version"}
     raw = ctypes.CDLL(ea.LIB_PATH)
     for n in names:
@@ -167,3 +167,20 @@ def test_bwd_validation():
     assert _bwd(ws=P + 5 * P2) == ea.ERR_VALUE        # workspace overlaps the LSE
     assert _bwd(B=0) == 0
     assert _bwd(N=0, q=None) == 0
+
+
+def _rq(x=P, x8=P + P2, s=P + 2 * P2, signs=None, c=P + 3 * P2, sn=P + 4 * P2, inter=1, B=1, H=2,
+        N=256, d=64, br=128):
+    return ea.lib().rope_blockquant_hadamard(x, x8, s, signs, c, sn, inter, B, H, N, d, br, None)
+
+
+def test_rope_blockquant_validation():
+    assert _rq(c=None) == ea.ERR_NULL
+    assert _rq(sn=None) == ea.ERR_NULL
+    assert _rq(x=None) == ea.ERR_NULL
+    assert _rq(inter=2) == ea.ERR_VALUE
+    assert _rq(br=64) == ea.ERR_VALUE
+    assert _rq(d=96) == ea.ERR_SHAPE
+    assert _rq(c=P + 3 * P2 + 4) == ea.ERR_ALIGN   # tables need 16-byte alignment
+    assert _rq(x8=P + 100 * 16) == ea.ERR_VALUE
+    assert _rq(N=0) == 0
