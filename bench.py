@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--bwd-reps", type=int, default=20,
                    help="timed launches of the bf16 gradients (attn_bwd_bf16) on the bf16 "
                         "workload, after the timed steps; 0 skips them")
+    p.add_argument("--rope-reps", type=int, default=20,
+                   help="timed launches of the RoPE-fused pre-pass on the fp8 workload's Q; 0 "
+                        "skips them")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run one plain 256 MiB device copy (untimed), the reference that "
                         "scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -273,6 +276,31 @@ def main():
             "ms": round(t_bwd * 1e3, 4), "reps": a.bwd_reps,
             "timing": "median of per-call HIP event times",
             "finite": bool(all(torch.isfinite(x).all().item() for x in (dq, dk, dv)))}
+    if a.rope_reps > 0:
+        # The pre-pass fused with a rotary embedding (half-split pairs), on the
+        # fp8 workload's Q; algorithmic bytes add the cos/sin tables, read once.
+        print(f"[bench] rope pre-pass: {a.rope_reps} launches", file=sys.stderr, flush=True)
+        rc, rsn = (torch.from_numpy(x).to(dev) for x in workloads.rope_tables(N, d))
+
+        def rq():
+            ea.rope_blockquant_hadamard(q8in, rc, rsn, False, signs, 128, out=codes[0],
+                                        scale=scales[0])
+        for _ in range(3):
+            rq()
+        rev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+               for _ in range(a.rope_reps)]
+        for e0, e1 in rev:
+            e0.record(stream)
+            rq()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        t_rq = float(np.median([e0.elapsed_time(e1) for e0, e1 in rev])) * 1e-3
+        rq_bytes = bq_bytes + 2 * N * (d // 2) * 4
+        out["rope_blockquant_hadamard"] = {
+            "workload": f"{w8.name} (Q), half-split RoPE", "gbps": round(rq_bytes / t_rq / 1e9, 1),
+            "pct_of_hbm_peak": round(100 * rq_bytes / t_rq / 1e9 / PEAK_HBM_GBS, 2),
+            "bytes_per_launch": rq_bytes, "us": round(t_rq * 1e6, 2),
+            "vs_plain_prepass_us": round(t_bq * 1e6, 2)}
     if not a.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w16, a.cpu_seconds)
