@@ -92,7 +92,7 @@ __device__ __forceinline__ void tile_compute(const char* smem, const uint32_t (&
   bf16x8 kf[NK];
   auto rd = [&](auto I) __attribute__((always_inline)) {
     constexpr int i = decltype(I)::value, t = i / 2, j = i % 2;
-    kf[i] = read_b128<ST * G::STAGE + j * 32 * G::RB>(kaddr[t]);
+    kf[i] = read_b128<G::koff(ST) + j * 32 * G::RB>(kaddr[t]);
   };
   static_for<AHEAD>(rd);
   f32x16 sacc[2];
@@ -104,19 +104,22 @@ __device__ __forceinline__ void tile_compute(const char* smem, const uint32_t (&
     if constexpr (i + AHEAD < NK) rd(IC<i + AHEAD>{});
   });
   // V^T fragments for this tile's P.V, read before the softmax so that the
-  // exp/sum work covers their latency.
-  bf16x8 vf[4][D / 32];
-  constexpr int VOFF = ST * G::STAGE + G::TILE;
-#pragma unroll
-  for (int e = 0; e < D / 32; ++e) {
-#define TR_PAIR(T2)                                                                              \
+  // exp/sum work covers their latency.  At d = 256 they come in two halves of
+  // four 32-row d-blocks (the second half after the first half's MFMAs), so
+  // at most 64 VGPRs of them are live.
+  constexpr int NEH = D / 32 <= 4 ? D / 32 : 4;  // d-blocks per half
+  constexpr int NHALF = (D / 32) / NEH;
+  bf16x8 vf[4][NEH];
+  constexpr int VOFF = G::voff(ST);
+#define TR_PAIR(T2, E, VA)                                                                       \
   {                                                                                              \
-    const bf16x4 lo = read_tr16<VOFF + (16 * (T2)) * G::RB>(vaddr[e]);                          \
-    const bf16x4 hi = read_tr16<VOFF + (16 * (T2) + 8) * G::RB>(vaddr[e]);                      \
-    vf[T2][e] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};                  \
+    const bf16x4 lo = read_tr16<VOFF + (16 * (T2)) * G::RB>(VA);                                \
+    const bf16x4 hi = read_tr16<VOFF + (16 * (T2) + 8) * G::RB>(VA);                            \
+    vf[T2][E] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};                  \
   }
-    TR_PAIR(0) TR_PAIR(1) TR_PAIR(2) TR_PAIR(3)
-#undef TR_PAIR
+#pragma unroll
+  for (int e = 0; e < NEH; ++e) {
+    TR_PAIR(0, e, vaddr[e]) TR_PAIR(1, e, vaddr[e]) TR_PAIR(2, e, vaddr[e]) TR_PAIR(3, e, vaddr[e])
   }
   if (MASKED) mask_s(sacc, k0, N, CAUSAL, qi, hh);
 
@@ -149,14 +152,27 @@ __device__ __forceinline__ void tile_compute(const char* smem, const uint32_t (&
 #pragma unroll
   for (int t2 = 0; t2 < 4; ++t2)
 #pragma unroll
-    for (int e = 0; e < D / 32; ++e) oacc[e] = mfma_bf16(vf[t2][e], pb[t2], oacc[e]);
+    for (int e = 0; e < NEH; ++e) oacc[e] = mfma_bf16(vf[t2][e], pb[t2], oacc[e]);
+  if constexpr (NHALF == 2) {
+#pragma unroll
+    for (int e = 0; e < NEH; ++e) {
+      TR_PAIR(0, e, vaddr[NEH + e]) TR_PAIR(1, e, vaddr[NEH + e])
+      TR_PAIR(2, e, vaddr[NEH + e]) TR_PAIR(3, e, vaddr[NEH + e])
+    }
+    lds_wait_v(vf);
+#pragma unroll
+    for (int t2 = 0; t2 < 4; ++t2)
+#pragma unroll
+      for (int e = 0; e < NEH; ++e) oacc[NEH + e] = mfma_bf16(vf[t2][e], pb[t2], oacc[NEH + e]);
+  }
+#undef TR_PAIR
 }
 
 // NW waves per workgroup (32 query rows each): 8 for long sequences (one
 // workgroup per CU, K/V tiles shared by 256 rows), 4 for short ones (two
 // workgroups per CU, so one's start-up and epilogue overlap the other's tiles).
 template <int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(64 * NW, 2) void attn_fwd_bf16_kernel(
+__global__ __launch_bounds__(64 * NW, D > 128 ? 1 : 2) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int H, int Hkv, int N, float scale_log2,
     int nqb, int xcd_remap) {
@@ -217,9 +233,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_bf16_kernel(
   do {                                                                                          \
     const uint32_t soff_ = (uint32_t)(k0) * row_bytes;                                          \
     _Pragma("unroll") for (int i_ = 0; i_ < LOADS; ++i_) {                                   \
-      char* dst_ = smem + (stage) * G::STAGE + (wave * LOADS + i_) * 1024;                   \
-      copy_to_lds16(rk, dst_, voff_k[i_], soff_);                                               \
-      copy_to_lds16(rv, dst_ + G::TILE, voff_v[i_], soff_);                                     \
+      char* dst_ = smem + (wave * LOADS + i_) * 1024;                                          \
+      copy_to_lds16(rk, dst_ + G::koff(stage), voff_k[i_], soff_);                              \
+      copy_to_lds16(rv, dst_ + G::VBASE + G::voff(stage), voff_v[i_], soff_);                   \
     }                                                                                           \
   } while (0)
 
@@ -236,7 +252,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int e = 0; e < D / 32; ++e) {
       const int c = 4 * e + 2 * (g & 1) + (q >> 1);
-      vaddr[e] = lds_addr(smem) + row * G::RB + ((c ^ G::swz_v(row)) * 16) + (q & 1) * 8;
+      vaddr[e] = lds_addr(smem) + G::VBASE + row * G::RB + ((c ^ G::swz_v(row)) * 16) + (q & 1) * 8;
     }
   }
 
@@ -315,9 +331,15 @@ hipError_t launch_nw(const void* q, const void* k, const void* v, void* o, float
 template <int D, bool CAUSAL>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                   int Hkv, int N, float scale, hipStream_t stream) {
-  const int small_n = (CAUSAL ? 4096 : 1024) * (128 / D);
-  if (N <= small_n) return launch_nw<D, CAUSAL, 4>(q, k, v, o, lse, B, H, Hkv, N, scale, stream);
-  return launch_nw<D, CAUSAL, 8>(q, k, v, o, lse, B, H, Hkv, N, scale, stream);
+  // d = 256: one wave per SIMD (Q fragments and O take 192 registers), so
+  // always four waves.
+  if constexpr (D > 128) {
+    return launch_nw<D, CAUSAL, 4>(q, k, v, o, lse, B, H, Hkv, N, scale, stream);
+  } else {
+    const int small_n = (CAUSAL ? 4096 : 1024) * (128 / D);
+    if (N <= small_n) return launch_nw<D, CAUSAL, 4>(q, k, v, o, lse, B, H, Hkv, N, scale, stream);
+    return launch_nw<D, CAUSAL, 8>(q, k, v, o, lse, B, H, Hkv, N, scale, stream);
+  }
 }
 
 }  // namespace
@@ -325,6 +347,9 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                                 int B, int H, int Hkv, int N, int d, bool causal,
                                 float softmax_scale, hipStream_t stream) {
+  if (d == 256)
+    return causal ? launch<256, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream)
+                  : launch<256, false>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream);
   if (d == 128)
     return causal ? launch<128, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream)
                   : launch<128, false>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream);

@@ -20,9 +20,15 @@ template <int D>
 struct Geo {
   static constexpr int RB = 2 * D;           // bytes per key row
   static constexpr int CPR = D / 8;          // 16-byte chunks per row
-  static constexpr int RP = 256 / RB;        // rows per 256-byte bank cycle
+  static constexpr int RP = RB >= 256 ? 1 : 256 / RB;  // rows per 256-byte bank cycle (>= 1)
   static constexpr int TILE = kBC * RB;      // bytes per K or V tile
   static constexpr int STAGE = 2 * TILE;     // K + V
+  // LDS byte offsets of stage st's K and V tiles.  d <= 128: stages are
+  // [K V][K V].  d = 256: [K0 K1][V0 V1], with the V region's base (VBASE)
+  // carried in the read addresses, so every immediate offset stays below 64 KB.
+  static constexpr int VBASE = D > 128 ? 2 * TILE : 0;
+  static constexpr int koff(int st) { return D > 128 ? st * TILE : st * STAGE; }
+  static constexpr int voff(int st) { return D > 128 ? st * TILE : st * STAGE + TILE; }
   // chunk position of chunk c of row `row`
   __device__ static int swz_k(int row) { return (row / RP) % CPR; }
   __device__ static int swz_v(int row) { return 4 * ((row / RP) % (CPR / 4)); }

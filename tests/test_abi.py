@@ -88,7 +88,9 @@ def test_attention_validation(fn):
     assert fn(q=None) == ea.ERR_NULL
     assert fn(o=None) == ea.ERR_NULL
     assert fn(d=96) == ea.ERR_SHAPE
-    assert fn(d=256) == ea.ERR_SHAPE
+    assert fn(d=512) == ea.ERR_SHAPE
+    # d = 256: the bf16 forward only
+    assert (fn(d=256, q=None) == ea.ERR_NULL) == (fn in (_bf16, _bf16g))
     assert fn(N=-1) == ea.ERR_SHAPE
     assert fn(B=-3) == ea.ERR_SHAPE
     assert fn(N=1 << 24) == ea.ERR_SHAPE
@@ -135,6 +137,7 @@ def test_blockquant_validation():
     assert _bq(x=None) == ea.ERR_NULL
     assert _bq(s=None) == ea.ERR_NULL
     assert _bq(d=32) == ea.ERR_SHAPE
+    assert _bq(d=256) == ea.ERR_SHAPE
     assert _bq(br=64) == ea.ERR_VALUE
     assert _bq(br=-1) == ea.ERR_VALUE
     assert _bq(x=P + 2) == ea.ERR_ALIGN
@@ -156,6 +159,7 @@ def test_bwd_validation():
     for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "ws"):
         assert _bwd(**{name: None}) == ea.ERR_NULL, name
     assert _bwd(d=96) == ea.ERR_SHAPE
+    assert _bwd(d=256) == ea.ERR_SHAPE
     assert _bwd(N=-1) == ea.ERR_SHAPE
     assert _bwd(scale=0.0) == ea.ERR_VALUE
     assert _bwd(causal=3) == ea.ERR_VALUE

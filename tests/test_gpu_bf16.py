@@ -212,3 +212,30 @@ def test_empty_problem_is_noop():
     z = torch.empty((0, 128, 2, 64), dtype=torch.bfloat16, device=DEV)
     o, lse = ea.attn_fwd_bf16(z, z, z)
     assert o.shape == z.shape and lse.numel() == 0
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 100, 129, 700])
+def test_d256_full_parity(causal, N):
+    """Head dim 256 (four one-wave-per-SIMD waves per workgroup; V^T fragments in
+    two halves); ragged N over several query and key tiles."""
+    w = workloads.Workload(f"d256_n{N}", 2, 2, N, 256, causal, seed=500 + N)
+    say(w.name + ("_causal" if causal else ""))
+    host, dev = bf16_inputs(w)
+    o, lse = _run(dev, causal, w.softmax_scale)
+    o_ref, lse_ref = oracle.naive_attention(*host, w.softmax_scale, causal)
+    absv, _ = oracle.naive_attention(host[0], host[1], np.abs(host[2]), w.softmax_scale, causal)
+    _check(o, lse, o_ref, lse_ref, w.name, absv)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_d256_full_size_sampled_rows(causal):
+    w = workloads.Workload("d256_b1h8n8192", 1, 8, 8192, 256, causal, seed=77)
+    say(w.name + ("_causal" if causal else ""))
+    host, dev = bf16_inputs(w)
+    o, lse = _run(dev, causal, w.softmax_scale)
+    rows = workloads.sample_rows(w.B, w.H, w.N, 384, seed=78)
+    o_ref, l_ref = oracle.naive_attention_rows(*host, w.softmax_scale, causal, rows)
+    absv, _ = oracle.naive_attention_rows(host[0], host[1], np.abs(host[2]), w.softmax_scale,
+                                          causal, rows)
+    _check(rows_of(o, rows), lse_rows(lse, rows), o_ref, l_ref, w.name, absv)

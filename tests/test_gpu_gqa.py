@@ -51,7 +51,7 @@ def _gate(o, lse, o_ref, lse_ref, tag):
 @pytest.mark.parametrize("N,d,H,Hkv,causal", [
     (200, 128, 6, 3, False), (200, 128, 6, 3, True),
     (1000, 64, 8, 1, False), (1000, 128, 4, 2, True),
-    (1500, 128, 8, 2, False), (1500, 64, 4, 1, True)])
+    (1500, 128, 8, 2, False), (1500, 64, 4, 1, True), (500, 256, 4, 2, True)])
 def test_bf16_gqa_full_parity(N, d, H, Hkv, causal):
     """Full oracle parity; N = 1500 takes the 8-wave workgroups, ragged tails."""
     tag = f"gqa_bf16_n{N}_d{d}_h{H}kv{Hkv}" + ("_causal" if causal else "")
