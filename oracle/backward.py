@@ -20,12 +20,16 @@ dO:
 
 (dS is the gradient with respect to the scores S = scale Q K^T that enter
 the softmax; its rows sum to zero because the rows of P sum to one.)
+
+With K and V on H_kv heads (grouped-query attention, [FA3-report] section
+3.4), query head h reads K/V head h // (H // H_kv), so the gradient of a K/V
+head is the sum of the per-query-head gradients of its group.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .attention import _heads
+from .attention import _heads, kv_head
 
 
 def _probs(qh, kh, scale, causal):
@@ -40,22 +44,24 @@ def _probs(qh, kh, scale, causal):
 
 def attention_backward(q, k, v, do, scale: float, causal: bool):
     """(dQ, dK, dV) as fp64 BSHD arrays for inputs q, k, v and output gradient
-    do (all BSHD, same shape)."""
+    do (BSHD; k, v may have H_kv heads, H a multiple of H_kv)."""
     qh, kh, vh, doh = _heads(q), _heads(k), _heads(v), _heads(do)
     B, H, N, d = qh.shape
+    Hkv = kh.shape[1]
     dq = np.empty_like(qh)
-    dk = np.empty_like(kh)
-    dv = np.empty_like(vh)
+    dk = np.zeros_like(kh)
+    dv = np.zeros_like(vh)
     for b in range(B):
         for h in range(H):
-            p = _probs(qh[b, h], kh[b, h], scale, causal)
-            o = p @ vh[b, h]
+            g = kv_head(h, H, Hkv)
+            p = _probs(qh[b, h], kh[b, g], scale, causal)
+            o = p @ vh[b, g]
             dd = np.sum(doh[b, h] * o, axis=1)
-            dv[b, h] = p.T @ doh[b, h]
-            dp = doh[b, h] @ vh[b, h].T
+            dv[b, g] += p.T @ doh[b, h]
+            dp = doh[b, h] @ vh[b, g].T
             ds = p * (dp - dd[:, None])
-            dq[b, h] = scale * (ds @ kh[b, h])
-            dk[b, h] = scale * (ds.T @ qh[b, h])
+            dq[b, h] = scale * (ds @ kh[b, g])
+            dk[b, g] += scale * (ds.T @ qh[b, h])
     back = lambda x: np.transpose(x, (0, 2, 1, 3))  # noqa: E731
     return back(dq), back(dk), back(dv)
 

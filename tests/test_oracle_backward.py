@@ -87,3 +87,25 @@ def test_heads_variant_equals_full():
     for f, p_ in zip(full, part):
         for r, (b, h) in enumerate(heads):
             np.testing.assert_array_equal(p_[r], f[b, :, h, :])
+
+
+def _torch_grads_gqa(q, k, v, do, scale, causal):
+    t = [torch.from_numpy(np.transpose(x, (0, 2, 1, 3)).copy()).requires_grad_(True)
+         for x in (q, k, v)]
+    o = torch.nn.functional.scaled_dot_product_attention(t[0], t[1], t[2], is_causal=causal,
+                                                         scale=scale, enable_gqa=True)
+    o.backward(torch.from_numpy(np.transpose(do, (0, 2, 1, 3)).copy()))
+    return [np.transpose(x.grad.numpy(), (0, 2, 1, 3)) for x in t]
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 2), (6, 1), (3, 3)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_matches_torch_autograd(H, Hkv, causal):
+    """K/V gradients of a grouped-query head are the sums over its group
+    (torch's enable_gqa attention differentiated by autograd)."""
+    q, do = _rand((2, 45, H, 16), 21), _rand((2, 45, H, 16), 22)
+    k, v = _rand((2, 45, Hkv, 16), 23), _rand((2, 45, Hkv, 16), 24)
+    got = attention_backward(q, k, v, do, 0.3, causal)
+    ref = _torch_grads_gqa(q, k, v, do, 0.3, causal)
+    for g, r in zip(got, ref):
+        np.testing.assert_allclose(g, r, rtol=1e-10, atol=1e-12)
