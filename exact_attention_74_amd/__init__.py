@@ -37,6 +37,7 @@ SIGNATURES = {
     "attn_fwd_bf16_gqa": [_c_void_p] * 5 + [_c_int] * 6 + [_c_float, _c_void_p],
     "attn_fwd_fp8_gqa": [_c_void_p] * 8 + [_c_int] * 6 + [_c_float, _c_void_p],
     "attn_bwd_bf16": [_c_void_p] * 10 + [_c_int] * 5 + [_c_float, _c_void_p],
+    "attn_bwd_bf16_gqa": [_c_void_p] * 10 + [_c_int] * 6 + [_c_float, _c_void_p],
     "attn_bwd_bf16_workspace_bytes": [_c_int] * 3,
     "rope_blockquant_hadamard": [_c_void_p] * 6 + [_c_int] * 6 + [_c_void_p],
     "blockquant_hadamard": [_c_void_p] * 4 + [_c_int] * 5 + [_c_void_p],
@@ -230,22 +231,25 @@ def attn_bwd_bf16(q, k, v, o, lse, do, causal: bool = False, softmax_scale: floa
                   dv: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
     """Gradients (dQ, dK, dV) of attn_fwd_bf16 given its output ``o``, its LSE and
     the output gradient ``do`` (all bf16 BSHD except the fp32 [B, H, N] LSE).
+    k and v may have H_kv heads (grouped-query); dk, dv then have H_kv heads.
 
     ``workspace``: optional float32 device tensor of at least
     attn_bwd_bf16_workspace_bytes(B, H, N) bytes; allocated here if omitted.
     """
     shape = _check_bshd("q", q, torch.bfloat16)
-    for name, t in (("k", k), ("v", v), ("o", o), ("do", do)):
+    for name, t in (("o", o), ("do", do)):
         if _check_bshd(name, t, torch.bfloat16) != shape:
             raise ValueError(f"{name} must have q's shape")
+    Hkv = _kv_heads("attn_bwd_bf16", shape, _check_bshd("k", k, torch.bfloat16),
+                    _check_bshd("v", v, torch.bfloat16), grouped=True)
     B, N, H, d = shape
     if (not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32
             or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous() or lse.device != q.device):
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
     nbytes = lib().attn_bwd_bf16_workspace_bytes(B, H, N)
     if nbytes < 0:
         raise ExattnError("attn_bwd_bf16_workspace_bytes", nbytes)
@@ -254,9 +258,9 @@ def attn_bwd_bf16(q, k, v, o, lse, do, causal: bool = False, softmax_scale: floa
     elif (workspace.dtype != torch.float32 or workspace.device != q.device
           or workspace.numel() * 4 < nbytes or not workspace.is_contiguous()):
         raise ValueError(f"workspace must be a contiguous float32 tensor of >= {nbytes} bytes")
-    _call("attn_bwd_bf16", q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-          lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
-          B, H, N, d, int(bool(causal)), scale, _stream_ptr(q))
+    _call("attn_bwd_bf16_gqa", q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+          do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+          workspace.data_ptr(), B, H, Hkv, N, d, int(bool(causal)), scale, _stream_ptr(q))
     return dq, dk, dv
 
 

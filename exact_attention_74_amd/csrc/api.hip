@@ -43,7 +43,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? EXATTN_OK : EXATTN_ERR_H
 
 extern "C" {
 
-int exattn_abi_version(void) { return 4; }
+int exattn_abi_version(void) { return 5; }
 
 const char* exattn_strerror(int code) {
   switch (code) {
@@ -123,11 +123,13 @@ long long attn_bwd_bf16_workspace_bytes(int B, int H, int N) {
   return 8LL * B * H * N;
 }
 
-int attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                  const float* lse, void* dq, void* dk, void* dv, float* workspace, int B, int H,
-                  int N, int d, int causal, float softmax_scale, void* stream) {
+int attn_bwd_bf16_gqa(const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                      float* workspace, int B, int H, int H_kv, int N, int d, int causal,
+                      float softmax_scale, void* stream) {
   int rc = check_shape(B, H, N, d, 2);
   if (rc) return rc;
+  if (!good_heads(H, H_kv)) return EXATTN_ERR_SHAPE;
   if ((causal != 0 && causal != 1) || !good_scale(softmax_scale)) return EXATTN_ERR_VALUE;
   // the per-row prep kernel runs 16 rows per workgroup
   if ((int64_t)B * N * H >= (int64_t(1) << 35)) return EXATTN_ERR_SHAPE;
@@ -141,11 +143,12 @@ int attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, co
     return EXATTN_ERR_ALIGN;
   const int64_t lse_bytes = (int64_t)B * H * N * 4;
   const int64_t ws_bytes = 2 * lse_bytes;
+  const int64_t kv_bytes = (int64_t)B * N * H_kv * d * 2;
   // Outputs and workspace must not overlap any input or each other.
   const void* in[] = {q, k, v, o, dout, lse};
-  const int64_t in_n[] = {bytes, bytes, bytes, bytes, bytes, lse_bytes};
+  const int64_t in_n[] = {bytes, kv_bytes, kv_bytes, bytes, bytes, lse_bytes};
   const void* out[] = {dq, dk, dv, workspace};
-  const int64_t out_n[] = {bytes, bytes, bytes, ws_bytes};
+  const int64_t out_n[] = {bytes, kv_bytes, kv_bytes, ws_bytes};
   for (int i = 0; i < 4; ++i) {
     for (int j = 0; j < 6; ++j)
       if (overlap(out[i], out_n[i], in[j], in_n[j])) return EXATTN_ERR_VALUE;
@@ -153,8 +156,15 @@ int attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, co
       if (overlap(out[i], out_n[i], out[j], out_n[j])) return EXATTN_ERR_VALUE;
   }
   return hip_status(exattn::launch_attn_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, workspace, B,
-                                                 H, N, d, causal != 0, softmax_scale,
+                                                 H, H_kv, N, d, causal != 0, softmax_scale,
                                                  (hipStream_t)stream));
+}
+
+int attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv, float* workspace, int B, int H,
+                  int N, int d, int causal, float softmax_scale, void* stream) {
+  return attn_bwd_bf16_gqa(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, H, N, d, causal,
+                           softmax_scale, stream);
 }
 
 int blockquant_hadamard(const void* x, void* x8, float* scale, const float* signs, int B, int H,

@@ -189,7 +189,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * kNWb, 2) void bwd_dq_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Drow,
-    __bf16* __restrict__ dQ, int H, int N, float scale_log2, float scale, int nqb, int xcd_remap) {
+    __bf16* __restrict__ dQ, int H, int Hkv, int N, float scale_log2, float scale, int nqb,
+    int xcd_remap) {
   using G = Geo<D>;
   constexpr int NF = D / 16, NE = D / 32;
   constexpr int LOADS = G::TILE / (1024 * kNWb);
@@ -219,12 +220,15 @@ __global__ __launch_bounds__(64 * kNWb, 2) void bwd_dq_kernel(
   const float lse2 = qi < N ? L2[(int64_t)bh * N + qi] : 0.f;
   const float dd = qi < N ? Drow[(int64_t)bh * N + qi] : 0.f;
 
-  const uint32_t nbytes = (uint32_t)(((int64_t)(N - 1) * rs + D) * 2);
+  // K/V head of this query head (grouped-query attention: H / Hkv per group)
+  const int64_t rs_kv = (int64_t)Hkv * D;
+  const int64_t kv_off = ((int64_t)b * N * Hkv + h / (H / Hkv)) * D;
+  const uint32_t nbytes = (uint32_t)(((int64_t)(N - 1) * rs_kv + D) * 2);
   const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(K + head_off), (short)0, nbytes, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(K + kv_off), (short)0, nbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(V + head_off), (short)0, nbytes, 0x00020000);
-  const uint32_t row_bytes = (uint32_t)(rs * 2);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(V + kv_off), (short)0, nbytes, 0x00020000);
+  const uint32_t row_bytes = (uint32_t)(rs_kv * 2);
   uint32_t voff_k[LOADS], voff_v[LOADS];
   copy_offsets<D, LOADS, 1>(wave, lane, row_bytes, voff_k);
   copy_offsets<D, LOADS, 0>(wave, lane, row_bytes, voff_v);
@@ -325,8 +329,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * kNWb, 1) void bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Drow,
-    __bf16* __restrict__ dK, __bf16* __restrict__ dV, int H, int N, float scale_log2, float scale,
-    int nkb, int xcd_remap) {
+    __bf16* __restrict__ dK, __bf16* __restrict__ dV, int H, int Hkv, int N, float scale_log2,
+    float scale, int nkb, int xcd_remap) {
   using G = Geo<D>;
   constexpr int NF = D / 16, NE = D / 32;
   constexpr int LOADS = G::TILE / (1024 * kNWb);
@@ -339,10 +343,13 @@ __global__ __launch_bounds__(64 * kNWb, 1) void bwd_dkdv_kernel(
   const int li = lane & 31, hh = lane >> 5;
   int L = blockIdx.x;
   if (xcd_remap) L = (L & 7) * (gridDim.x >> 3) + (L >> 3);
-  const int kblk = L % nkb, bh = L / nkb;  // causal: low key blocks see the most queries
-  const int b = bh / H, h = bh - b * H;
-  const int64_t rs = (int64_t)H * D;
-  const int64_t head_off = ((int64_t)b * N * H + h) * D;
+  // One workgroup per (b, K/V head, 128 keys); it accumulates the gradients
+  // of all H / Hkv query heads that read this K/V head.
+  const int kblk = L % nkb, bhk = L / nkb;  // causal: low key blocks see the most queries
+  const int b = bhk / Hkv, hk = bhk - b * Hkv;
+  const int grp = H / Hkv;
+  const int64_t rs = (int64_t)H * D, rs_kv = (int64_t)Hkv * D;
+  const int64_t kv_off = ((int64_t)b * N * Hkv + hk) * D;
   const int k0w = kblk * kRowsB + wave * 32;  // this wave's first key
   const int kj = k0w + li;                    // this lane's key (MFMA column)
 
@@ -351,19 +358,23 @@ __global__ __launch_bounds__(64 * kNWb, 1) void bwd_dkdv_kernel(
 #pragma unroll
   for (int t = 0; t < NF; ++t) {
     const bf16x8 z = {};
-    kt[t] = kj < N ? *(const bf16x8*)(K + head_off + (int64_t)kj * rs + 16 * t + 8 * hh) : z;
-    vt[t] = kj < N ? *(const bf16x8*)(V + head_off + (int64_t)kj * rs + 16 * t + 8 * hh) : z;
+    kt[t] = kj < N ? *(const bf16x8*)(K + kv_off + (int64_t)kj * rs_kv + 16 * t + 8 * hh) : z;
+    vt[t] = kj < N ? *(const bf16x8*)(V + kv_off + (int64_t)kj * rs_kv + 16 * t + 8 * hh) : z;
   }
 
   const uint32_t nbytes = (uint32_t)(((int64_t)(N - 1) * rs + D) * 2);
-  const __amdgpu_buffer_rsrc_t rq =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(Q + head_off), (short)0, nbytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rg =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(dO + head_off), (short)0, nbytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(L2 + (int64_t)bh * N), (short)0, (uint32_t)N * 4, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(Drow + (int64_t)bh * N), (short)0, (uint32_t)N * 4, 0x00020000);
+  // Q, dO, LSE and D of query head h (set per head of the group)
+  __amdgpu_buffer_rsrc_t rq, rg, rl, rd;
+  auto set_head = [&](int h) __attribute__((always_inline)) {
+    const int64_t head_off = ((int64_t)b * N * H + h) * D;
+    const int64_t bh = (int64_t)b * H + h;
+    rq = __builtin_amdgcn_make_buffer_rsrc((void*)(Q + head_off), (short)0, nbytes, 0x00020000);
+    rg = __builtin_amdgcn_make_buffer_rsrc((void*)(dO + head_off), (short)0, nbytes, 0x00020000);
+    rl = __builtin_amdgcn_make_buffer_rsrc((void*)(L2 + bh * N), (short)0, (uint32_t)N * 4,
+                                           0x00020000);
+    rd = __builtin_amdgcn_make_buffer_rsrc((void*)(Drow + bh * N), (short)0, (uint32_t)N * 4,
+                                           0x00020000);
+  };
   const uint32_t row_bytes = (uint32_t)(rs * 2);
   uint32_t voff[LOADS];
   copy_offsets<D, LOADS, 1>(wave, lane, row_bytes, voff);
@@ -472,24 +483,29 @@ __global__ __launch_bounds__(64 * kNWb, 1) void bwd_dkdv_kernel(
         tile(IC<ST_>{}, IC<0>{}, i0_);                                                          \
     }                                                                                           \
   } while (0)
-  load_tile(0, qt0 * kBC);
-  int qt = qt0;
-  for (; qt + 1 < nqt; qt += 2) {
-    STEP(0, qt);
-    STEP(1, qt + 1);
+  for (int g = 0; g < grp; ++g) {
+    set_head(hk * grp + g);
+    // every wave is done with the previous head's tiles before stage 0 is refilled
+    if (g > 0) __syncthreads();
+    load_tile(0, qt0 * kBC);
+    int qt = qt0;
+    for (; qt + 1 < nqt; qt += 2) {
+      STEP(0, qt);
+      STEP(1, qt + 1);
+    }
+    if (qt < nqt) STEP(0, qt);
   }
-  if (qt < nqt) STEP(0, qt);
 #undef STEP
   if (kj < N) {
-    store_rows<D>(dK + head_off + (int64_t)kj * rs, dkacc, scale, hh);
-    store_rows<D>(dV + head_off + (int64_t)kj * rs, dvacc, 1.f, hh);
+    store_rows<D>(dK + kv_off + (int64_t)kj * rs_kv, dkacc, scale, hh);
+    store_rows<D>(dV + kv_off + (int64_t)kj * rs_kv, dvacc, 1.f, hh);
   }
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                       const float* lse, void* dq, void* dk, void* dv, float* ws, int B, int H,
-                      int N, float scale, hipStream_t stream) {
+                      int Hkv, int N, float scale, hipStream_t stream) {
   const int64_t rows = (int64_t)B * N * H;
   float* drow = ws;
   float* l2 = ws + rows;
@@ -497,14 +513,16 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
                      stream, (const __bf16*)o, (const __bf16*)dout, lse, drow, l2, H, N, rows);
   const int nb = (N + kRowsB - 1) / kRowsB;
+  const int64_t grid_kv = (int64_t)B * Hkv * nb;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)grid_kv), dim3(64 * kNWb), 0,
+                     stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
+                     (const __bf16*)dout, l2, drow, (__bf16*)dk, (__bf16*)dv, H, Hkv, N,
+                     scale * kLog2e, scale, nb, (grid_kv % 8 == 0) ? 1 : 0);
   const int64_t grid = (int64_t)B * H * nb;
-  const int remap = (grid % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(64 * kNWb), 0, stream,
-                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, l2,
-                     drow, (__bf16*)dk, (__bf16*)dv, H, N, scale * kLog2e, scale, nb, remap);
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(64 * kNWb), 0, stream,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, l2,
-                     drow, (__bf16*)dq, H, N, scale * kLog2e, scale, nb, remap);
+                     drow, (__bf16*)dq, H, Hkv, N, scale * kLog2e, scale, nb,
+                     (grid % 8 == 0) ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -512,16 +530,16 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
 
 hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                                 const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                                float* workspace, int B, int H, int N, int d, bool causal,
-                                float softmax_scale, hipStream_t stream) {
+                                float* workspace, int B, int H, int Hkv, int N, int d,
+                                bool causal, float softmax_scale, hipStream_t stream) {
   if (d == 128)
-    return causal ? launch_bwd<128, true>(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N,
+    return causal ? launch_bwd<128, true>(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, Hkv, N,
                                           softmax_scale, stream)
-                  : launch_bwd<128, false>(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N,
+                  : launch_bwd<128, false>(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, Hkv, N,
                                            softmax_scale, stream);
-  return causal ? launch_bwd<64, true>(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N,
+  return causal ? launch_bwd<64, true>(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, Hkv, N,
                                        softmax_scale, stream)
-                : launch_bwd<64, false>(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N,
+                : launch_bwd<64, false>(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, Hkv, N,
                                         softmax_scale, stream);
 }
 

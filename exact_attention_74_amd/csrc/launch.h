@@ -17,11 +17,12 @@ hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* v8, c
                                int Hkv, int N, int d, bool causal, float softmax_scale,
                                hipStream_t stream);
 
-// Gradients of the bf16 forward; workspace: 2 B H N floats (D, LSE*log2e).
+// Gradients of the bf16 forward; workspace: 2 B H N floats (D, LSE*log2e);
+// K/V (and dK/dV) on Hkv heads.
 hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                                 const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                                float* workspace, int B, int H, int N, int d, bool causal,
-                                float softmax_scale, hipStream_t stream);
+                                float* workspace, int B, int H, int Hkv, int N, int d,
+                                bool causal, float softmax_scale, hipStream_t stream);
 
 hipError_t launch_blockquant(const void* x, void* x8, float* scale, const float* signs, int B, int H,
                              int N, int d, int block_rows, hipStream_t stream);

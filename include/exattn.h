@@ -132,6 +132,16 @@ long long attn_bwd_bf16_workspace_bytes(int B, int H, int N);
 int attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dout,
                   const float* lse, void* dq, void* dk, void* dv, float* workspace,
                   int B, int H, int N, int d, int causal, float softmax_scale, void* stream);
+/*
+ * The same for grouped-query / multi-query attention: k, v, dk, dv on H_kv
+ * heads ([B, N, H_kv, d]; H a multiple of H_kv, query head h reads K/V head
+ * h / (H / H_kv)); dk and dv are the sums over each K/V head's group of query
+ * heads.  attn_bwd_bf16 is this with H_kv = H.
+ */
+int attn_bwd_bf16_gqa(const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                      float* workspace, int B, int H, int H_kv, int N, int d, int causal,
+                      float softmax_scale, void* stream);
 
 /*
  * FP8 pre-pass: optional incoherent rotation, then block quantisation to e4m3

@@ -31,13 +31,14 @@ def _codes():
 
 def test_library_builds_and_loads():
     assert os.path.exists(ea.LIB_PATH)
-    assert ea.lib().exattn_abi_version() == 4
+    assert ea.lib().exattn_abi_version() == 5
 
 
 def test_exports_every_declared_symbol():
     names = _declared()
     assert set(names) == {"attn_fwd_bf16", "attn_fwd_fp8", "attn_fwd_bf16_gqa", "attn_fwd_fp8_gqa",
-                          "attn_bwd_bf16", "attn_bwd_bf16_workspace_bytes", "rope_blockquant_hadamard",
+                          "attn_bwd_bf16", "attn_bwd_bf16_gqa", "attn_bwd_bf16_workspace_bytes",
+                          "rope_blockquant_hadamard",
                           "blockquant_hadamard", "exattn_strerror", "exattn_abi_version"}
     raw = ctypes.CDLL(ea.LIB_PATH)
     for n in names:
@@ -188,3 +189,12 @@ def test_rope_blockquant_validation():
     assert _rq(c=P + 3 * P2 + 4) == ea.ERR_ALIGN   # tables need 16-byte alignment
     assert _rq(x8=P + 100 * 16) == ea.ERR_VALUE
     assert _rq(N=0) == 0
+
+
+def test_bwd_gqa_head_counts():
+    f = ea.lib().attn_bwd_bf16_gqa
+    args = [P, P + P2, P + 2 * P2, P + 3 * P2, P + 4 * P2, P + 5 * P2, P + 6 * P2, P + 7 * P2,
+            P + 8 * P2, P + 9 * P2]
+    assert f(*args, 1, 4, 3, 256, 64, 0, 0.125, None) == ea.ERR_SHAPE
+    assert f(*args, 1, 4, 0, 256, 64, 0, 0.125, None) == ea.ERR_SHAPE
+    assert f(*args, 0, 4, 2, 256, 64, 0, 0.125, None) == 0

@@ -146,3 +146,32 @@ def test_bwd_empty_is_noop():
     dq, dk, dv = ea.attn_bwd_bf16(z, z, z, z, lse, z)
     torch.cuda.synchronize()
     assert dq.numel() == 0
+
+
+@pytest.mark.parametrize("H,Hkv,N,d,causal", [(4, 2, 300, 128, False), (4, 2, 300, 128, True),
+                                               (6, 1, 500, 64, True), (8, 2, 1000, 128, False)])
+def test_bwd_gqa_full_parity(H, Hkv, N, d, causal):
+    """Grouped-query gradients: dK, dV of a K/V head sum over its group.  The
+    bound is the per-query-head bound (K/V written out per head) summed over
+    the group."""
+    tag = f"bwd_gqa_h{H}kv{Hkv}_n{N}_d{d}" + ("_causal" if causal else "")
+    say(tag)
+    w = workloads.Workload("bwdg", 2, H, N, d, False, seed=600 + N + H)
+    q = workloads.to_bf16_f32(workloads.gen_qkv(w)[0])
+    k, v = (workloads.to_bf16_f32(x) for x in workloads.gen_qkv_gqa(2, N, H, Hkv, d, 610 + N)[1:])
+    do = workloads.to_bf16_f32(workloads.gen_random((2, N, H, d), 620 + N))
+    scale = d ** -0.5
+    qd, kd, vd, dod = (_dev(x) for x in (q, k, v, do))
+    o, lse = ea.attn_fwd_bf16_gqa(qd, kd, vd, causal=causal, softmax_scale=scale)
+    dq, dk, dv = ea.attn_bwd_bf16(qd, kd, vd, o, lse, dod, causal=causal, softmax_scale=scale)
+    torch.cuda.synchronize()
+    got = [to_np(x) for x in (dq, dk, dv)]
+    assert got[1].shape == k.shape and got[2].shape == v.shape
+    ref = oracle.attention_backward(q, k, v, do, scale, causal)
+    r = H // Hkv
+    kr, vr = (np.repeat(x, r, axis=2) for x in (k, v))
+    bq, bk, bv = _bounds(q, kr, vr, do, to_np(o), scale, causal)
+    B_, N_ = bk.shape[0], bk.shape[1]
+    bk = bk.reshape(B_, N_, Hkv, r, d).sum(axis=3)
+    bv = bv.reshape(B_, N_, Hkv, r, d).sum(axis=3)
+    _check(got, ref, (bq, bk, bv), tag)
