@@ -22,7 +22,7 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
 // elt: bytes per element of the Q/K/V inputs.  One batch entry of a tensor
 // (N x H x d elements) must stay below 2 GiB: kernels address a head's rows
 // with 32-bit buffer offsets.
-int check_shape(int B, int H, int N, int d, int elt, bool allow_d256 = false) {
+int check_shape(int B, int H, int N, int d, int elt, bool allow_d256 = true) {
   if (B < 0 || H < 0 || N < 0) return EXATTN_ERR_SHAPE;
   if (d != 64 && d != 128 && !(allow_d256 && d == 256)) return EXATTN_ERR_SHAPE;
   if ((int64_t)N >= kMaxN) return EXATTN_ERR_SHAPE;
@@ -43,14 +43,14 @@ int hip_status(hipError_t e) { return e == hipSuccess ? EXATTN_OK : EXATTN_ERR_H
 
 extern "C" {
 
-int exattn_abi_version(void) { return 5; }
+int exattn_abi_version(void) { return 6; }
 
 const char* exattn_strerror(int code) {
   switch (code) {
     case EXATTN_OK: return "success";
     case EXATTN_ERR_NULL: return "a required pointer is NULL";
     case EXATTN_ERR_SHAPE:
-      return "unsupported shape (negative size, d not in {64,128} (bf16 forward: also 256), too "
+      return "unsupported shape (negative size, d not in {64,128,256} (backward: {64,128}), too "
              "large, or H not a multiple of H_kv)";
     case EXATTN_ERR_ALIGN: return "pointer not aligned (tensors 16 bytes, scales/LSE 4 bytes)";
     case EXATTN_ERR_VALUE: return "invalid value (softmax_scale, causal, block_rows, or aliasing output)";
@@ -62,7 +62,7 @@ const char* exattn_strerror(int code) {
 int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                       int H, int H_kv, int N, int d, int causal, float softmax_scale,
                       void* stream) {
-  int rc = check_shape(B, H, N, d, 2, /*allow_d256=*/true);
+  int rc = check_shape(B, H, N, d, 2);
   if (rc) return rc;
   if (!good_heads(H, H_kv)) return EXATTN_ERR_SHAPE;
   if ((causal != 0 && causal != 1) || !good_scale(softmax_scale)) return EXATTN_ERR_VALUE;
@@ -127,7 +127,7 @@ int attn_bwd_bf16_gqa(const void* q, const void* k, const void* v, const void* o
                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
                       float* workspace, int B, int H, int H_kv, int N, int d, int causal,
                       float softmax_scale, void* stream) {
-  int rc = check_shape(B, H, N, d, 2);
+  int rc = check_shape(B, H, N, d, 2, /*allow_d256=*/false);
   if (rc) return rc;
   if (!good_heads(H, H_kv)) return EXATTN_ERR_SHAPE;
   if ((causal != 0 && causal != 1) || !good_scale(softmax_scale)) return EXATTN_ERR_VALUE;

@@ -2,8 +2,9 @@
 // of the FlashAttention-3 report, section 3.3, on v_mfma_f32_32x32x64_f8f6f4.
 //
 // Decomposition as in the bf16 kernel: one workgroup of 8 waves per (b, h,
-// block of 256 query rows), 32 query rows per wave, two waves per SIMD; the
-// keys are streamed 128 at a time, so every key tile is exactly one
+// block of 256 query rows), 32 query rows per wave, two waves per SIMD (head
+// dim 256: 4 waves and 128 rows, one wave per SIMD with its 512 registers);
+// the keys are streamed 128 at a time, so every key tile is exactly one
 // quantisation block and every wave's rows lie in one query block:
 //   * S block scaling: the tile's scalar q_scale * k_scale * softmax_scale *
 //     log2(e) multiplies the fp32 accumulator inside the exp2 argument.
@@ -29,25 +30,36 @@
 namespace exattn {
 namespace {
 
-constexpr int kBR = 256;
 constexpr int kBC = 128;  // keys per tile = rows per quantisation block
 constexpr int kQB = 128;  // rows per quantisation block
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
+
+// Waves per workgroup (32 query rows each).
+template <int D>
+constexpr int waves() { return D > 128 ? 4 : 8; }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
 template <int D>
 struct Geo8 {
+  static constexpr int NW = waves<D>();
   static constexpr int RB = D;                // bytes per key row
   static constexpr int CPR = D / 16;          // 16-byte chunks per row
   static constexpr int RP = 256 / RB;         // rows per 256-byte bank cycle
   static constexpr int TILE = kBC * RB;       // bytes per K or V tile
   static constexpr int STAGE = 2 * TILE;      // K + V
-  static constexpr int LOADS = TILE / (1024 * kWaves);
-  // chunk c of row `row` is stored at chunk position c ^ swz(row)
+  static constexpr int LOADS = TILE / (1024 * NW);
+  // LDS layout: [K0 V0 K1 V1] up to d = 128; [K0 K1 V0 V1] at d = 256, with
+  // the V region's base in the read addresses, so that every read offset is a
+  // 16-bit immediate.
+  static constexpr int VBASE = D > 128 ? 2 * TILE : 0;
+  static constexpr int koff(int st) { return D > 128 ? st * TILE : st * STAGE; }
+  static constexpr int voff(int st) { return D > 128 ? st * TILE : st * STAGE + TILE; }
+  // chunk c of row `row` is stored at chunk position c ^ swz(row).  The V
+  // swizzle spreads the eight rows (and two chunks) one transposed read
+  // instruction touches per half-wave over distinct banks.
   __device__ static int swz_k(int row) { return (row / RP) % CPR; }
   __device__ static int swz_v(int row) {
+    if (D == 256) return 2 * ((row & 3) | (((row >> 3) & 1) << 2));
     if (D == 128) return 2 * (((row >> 1) & 1) | (((row >> 3) & 1) << 1));
     return 2 * ((row >> 3) & 1);
   }
@@ -79,7 +91,7 @@ __device__ __forceinline__ i32x2 read_tr8(uint32_t addr) {
 // that no use of them is scheduled before the wait.
 template <int NE>
 __device__ __forceinline__ void lds_wait_v(i32x8 (&vf)[2][NE]) {
-  static_assert(NE == 4 || NE == 2, "d = 128 or 64");
+  static_assert(NE == 4 || NE == 2, "four or two 32-dim blocks");
   if constexpr (NE == 4)
     asm volatile("s_waitcnt lgkmcnt(0)"
                  : "+v"(vf[0][0]), "+v"(vf[0][1]), "+v"(vf[0][2]), "+v"(vf[0][3]),
@@ -102,12 +114,13 @@ __device__ __forceinline__ void mask_s8(f32x16 (&sacc)[4], int k0, int N, bool c
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
+__global__ __launch_bounds__(64 * waves<D>(), 1) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
     const float* __restrict__ SQ, const float* __restrict__ SK, const float* __restrict__ SV,
     __bf16* __restrict__ O, float* __restrict__ LSE, int H, int Hkv, int N, float scale_log2,
     int nqb, int xcd_remap) {
   using G = Geo8<D>;
+  constexpr int kBR = 32 * G::NW;  // query rows per workgroup
   __shared__ __attribute__((aligned(1024))) char smem[2 * G::STAGE];
 
   const int tid = threadIdx.x;
@@ -164,9 +177,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   do {                                                                                          \
     const uint32_t soff_ = (uint32_t)(k0) * row_bytes;                                          \
     _Pragma("unroll") for (int i_ = 0; i_ < G::LOADS; ++i_) {                                   \
-      char* dst_ = smem + (stage) * G::STAGE + (wave * G::LOADS + i_) * 1024;                   \
-      copy_to_lds16(rk, dst_, voff_k[i_], soff_);                                               \
-      copy_to_lds16(rv, dst_ + G::TILE, voff_v[i_], soff_);                                     \
+      char* dst_ = smem + (wave * G::LOADS + i_) * 1024;                                        \
+      copy_to_lds16(rk, dst_ + G::koff(stage), voff_k[i_], soff_);                              \
+      copy_to_lds16(rv, dst_ + G::VBASE + G::voff(stage), voff_v[i_], soff_);                   \
     }                                                                                           \
   } while (0)
 
@@ -179,7 +192,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
       kaddr[t][c] = li * G::RB + (((4 * t + 2 * hh + c) ^ G::swz_k(li)) * 16);
   // V^T operand, transposed read r of k-step u: source lane 2j + q of group g
   // points at key 64u + 16r + 8(j/4) + 4(g/2) + j%4, dims 32e + 16(g%2) + 8q.
-  uint32_t vaddr[D / 32];  // LDS addresses in stage 0's V buffer
+  uint32_t vaddr[D / 32];  // LDS addresses relative to a V buffer (stage offset: immediate)
   {
     const int src = lane & 15, g = lane >> 4;
     const int j = src >> 1, q = src & 1;
@@ -187,7 +200,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
 #pragma unroll
     for (int e = 0; e < D / 32; ++e) {
       const int c = 2 * e + (g & 1);
-      vaddr[e] = lds_addr(smem) + G::TILE + kl * G::RB + ((c ^ G::swz_v(kl)) * 16) + 8 * q;
+      vaddr[e] = lds_addr(smem) + G::VBASE + kl * G::RB + ((c ^ G::swz_v(kl)) * 16) + 8 * q;
     }
   }
 
@@ -198,6 +211,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
 #pragma unroll
   for (int e = 0; e < D / 32; ++e) oacc[e] = f32x16{};
 
+  constexpr int NEH = D / 32 <= 4 ? D / 32 : 4;  // 32-dim blocks of O per half
+  constexpr int NHALF = (D / 32) / NEH;
   const int nkb_all = ceil_div(N, kBC);
   const int nkb = CAUSAL ? min(nkb_all, ceil_div(min(N, (qblk + 1) * kBR), kBC)) : nkb_all;
 
@@ -207,7 +222,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   // both loops take tiles in pairs from an even index, so ST is a
   // compile-time constant and every LDS offset an immediate.
 #define TILE_BODY(ST, MASKED)                                                                        \
-    const char* kt = smem + (ST) * G::STAGE;                                                         \
+    const char* kt = smem + G::koff(ST);                                                             \
                                                                                                      \
     i32x8 kf[4][D / 64];                                                                             \
 _Pragma("unroll")                                                                                    \
@@ -265,28 +280,33 @@ _Pragma("unroll")                                                               
 _Pragma("unroll")                                                                                    \
     for (int e = 0; e < D / 32; ++e) oacc[e] *= f;                                                   \
                                                                                                      \
-    i32x8 vf[2][D / 32];                                                                             \
+    /* V^T operands in halves of at most four 32-dim blocks (d = 256: two) */                      \
 _Pragma("unroll")                                                                                    \
-    for (int e = 0; e < D / 32; ++e) {                                                               \
-      const uint32_t va = vaddr[e];                                                                  \
-      i32x2 r[8];                                                                                    \
-      r[0] = read_tr8<(ST) * G::STAGE + 0 * G::RB>(va);                                              \
-      r[1] = read_tr8<(ST) * G::STAGE + 16 * G::RB>(va);                                             \
-      r[2] = read_tr8<(ST) * G::STAGE + 32 * G::RB>(va);                                             \
-      r[3] = read_tr8<(ST) * G::STAGE + 48 * G::RB>(va);                                             \
-      r[4] = read_tr8<(ST) * G::STAGE + 64 * G::RB>(va);                                             \
-      r[5] = read_tr8<(ST) * G::STAGE + 80 * G::RB>(va);                                             \
-      r[6] = read_tr8<(ST) * G::STAGE + 96 * G::RB>(va);                                             \
-      r[7] = read_tr8<(ST) * G::STAGE + 112 * G::RB>(va);                                            \
-      vf[0][e] = i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};      \
-      vf[1][e] = i32x8{r[4][0], r[4][1], r[5][0], r[5][1], r[6][0], r[6][1], r[7][0], r[7][1]};      \
-    }                                                                                                \
-    lds_wait_v(vf);                                                                                  \
+    for (int hf = 0; hf < NHALF; ++hf) {                                                             \
+      i32x8 vf[2][NEH];                                                                              \
+_Pragma("unroll")                                                                                    \
+      for (int e = 0; e < NEH; ++e) {                                                                \
+        const uint32_t va = vaddr[hf * NEH + e];                                                     \
+        i32x2 r[8];                                                                                  \
+        r[0] = read_tr8<G::voff(ST) + 0 * G::RB>(va);                                                \
+        r[1] = read_tr8<G::voff(ST) + 16 * G::RB>(va);                                               \
+        r[2] = read_tr8<G::voff(ST) + 32 * G::RB>(va);                                               \
+        r[3] = read_tr8<G::voff(ST) + 48 * G::RB>(va);                                               \
+        r[4] = read_tr8<G::voff(ST) + 64 * G::RB>(va);                                               \
+        r[5] = read_tr8<G::voff(ST) + 80 * G::RB>(va);                                               \
+        r[6] = read_tr8<G::voff(ST) + 96 * G::RB>(va);                                               \
+        r[7] = read_tr8<G::voff(ST) + 112 * G::RB>(va);                                              \
+        vf[0][e] = i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};    \
+        vf[1][e] = i32x8{r[4][0], r[4][1], r[5][0], r[5][1], r[6][0], r[6][1], r[7][0], r[7][1]};    \
+      }                                                                                              \
+      lds_wait_v(vf);                                                                                \
                                                                                                      \
 _Pragma("unroll")                                                                                    \
-    for (int u = 0; u < 2; ++u)                                                                      \
+      for (int u = 0; u < 2; ++u)                                                                    \
 _Pragma("unroll")                                                                                    \
-      for (int e = 0; e < D / 32; ++e) oacc[e] = mfma_fp8(vf[u][e], pf[u], oacc[e]);                 \
+        for (int e = 0; e < NEH; ++e)                                                                \
+          oacc[hf * NEH + e] = mfma_fp8(vf[u][e], pf[u], oacc[hf * NEH + e]);                        \
+    }                                                                                                \
 
 #define STEP8(ST, KB, MASKED)                                                                        \
   do {                                                                                               \
@@ -335,10 +355,11 @@ template <int D, bool CAUSAL>
 hipError_t launch(const void* q8, const void* k8, const void* v8, const float* sq, const float* sk,
                   const float* sv, void* o, float* lse, int B, int H, int Hkv, int N,
                   float scale, hipStream_t stream) {
+  constexpr int kBR = 32 * waves<D>();
   const int nqb = (N + kBR - 1) / kBR;
   const int64_t grid = (int64_t)B * H * nqb;
   const int remap = (grid % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(64 * waves<D>()), 0,
                      stream, (const uint8_t*)q8, (const uint8_t*)k8, (const uint8_t*)v8, sq, sk, sv,
                      (__bf16*)o, lse, H, Hkv, N, scale * kLog2e, nqb, remap);
   return hipGetLastError();
@@ -350,6 +371,9 @@ hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* v8, c
                                const float* sk, const float* sv, void* o, float* lse, int B, int H,
                                int Hkv, int N, int d, bool causal, float softmax_scale,
                                hipStream_t stream) {
+  if (d == 256)
+    return causal ? launch<256, true>(q8, k8, v8, sq, sk, sv, o, lse, B, H, Hkv, N, softmax_scale, stream)
+                  : launch<256, false>(q8, k8, v8, sq, sk, sv, o, lse, B, H, Hkv, N, softmax_scale, stream);
   if (d == 128)
     return causal ? launch<128, true>(q8, k8, v8, sq, sk, sv, o, lse, B, H, Hkv, N, softmax_scale, stream)
                   : launch<128, false>(q8, k8, v8, sq, sk, sv, o, lse, B, H, Hkv, N, softmax_scale, stream);

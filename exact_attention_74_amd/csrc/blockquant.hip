@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void blockquant_kernel(const __bf16* __re
                                                               const float* __restrict__ rsin,
                                                               int H, int N, int nsb, float kconst) {
   constexpr int LPR = 4;                 // lanes per row
-  constexpr int EPL = D / LPR;           // elements per lane (32 or 16)
+  constexpr int EPL = D / LPR;           // elements per lane (64, 32 or 16)
   constexpr int RPP = kThreads / LPR;    // rows per pass
   constexpr int PASSES = kRows / RPP;
   __shared__ float red[kThreads / 64];
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void blockquant_kernel(const __bf16* __re
       for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int k = 0; k < 8; ++k) y[p][c][k] = __builtin_fmaf(sg16, y[p][c][k], quad_xor<2>(y[p][c][k]));
-      // strides 32, 64: across this lane's chunks
+      // strides 32, 64 (, 128): across this lane's chunks
 #pragma unroll
       for (int st = 1; st < NC; st <<= 1)
 #pragma unroll
@@ -273,6 +273,11 @@ hipError_t dispatch(const void* x, void* x8, float* scale, const float* signs, c
                     const float* rsin, int B, int H, int N, int d, int block_rows,
                     hipStream_t stream) {
   const bool rot = signs != nullptr;
+  if (d == 256)
+    return rot ? launch<256, true, ROPE>(x, x8, scale, signs, rcos, rsin, B, H, N, block_rows,
+                                         stream)
+               : launch<256, false, ROPE>(x, x8, scale, signs, rcos, rsin, B, H, N, block_rows,
+                                          stream);
   if (d == 128)
     return rot ? launch<128, true, ROPE>(x, x8, scale, signs, rcos, rsin, B, H, N, block_rows,
                                          stream)

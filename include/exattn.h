@@ -22,8 +22,8 @@
  *               Element (b, n, h, c) is at ((b*N + n)*H + h)*d + c.
  *   Sizes       B, H, N >= 0 (any of them 0: nothing to do, returns 0 once
  *               the sizes and values are valid; pointers may then be NULL);
- *               d in {64, 128}, and also 256 for the bf16 forward (other head
- *               dims are zero-padded by the caller to the next of these,
+ *               d in {64, 128, 256}; the backward takes d in {64, 128} (other
+ *               head dims are zero-padded by the caller to the next of these,
  *               keeping softmax_scale = 1/sqrt(d_original); the same blog,
  *               section 3.1); B*H*ceil(N/128) < 2^31; N < 2^24;
  *               N*H*d*(bytes per input element) < 2^31 (one batch entry of

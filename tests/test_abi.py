@@ -31,7 +31,7 @@ def _codes():
 
 def test_library_builds_and_loads():
     assert os.path.exists(ea.LIB_PATH)
-    assert ea.lib().exattn_abi_version() == 5
+    assert ea.lib().exattn_abi_version() == 6
 
 
 def test_exports_every_declared_symbol():
@@ -90,8 +90,7 @@ def test_attention_validation(fn):
     assert fn(o=None) == ea.ERR_NULL
     assert fn(d=96) == ea.ERR_SHAPE
     assert fn(d=512) == ea.ERR_SHAPE
-    # d = 256: the bf16 forward only
-    assert (fn(d=256, q=None) == ea.ERR_NULL) == (fn in (_bf16, _bf16g))
+    assert fn(d=256, q=None) == ea.ERR_NULL  # d = 256 passes the shape check
     assert fn(N=-1) == ea.ERR_SHAPE
     assert fn(B=-3) == ea.ERR_SHAPE
     assert fn(N=1 << 24) == ea.ERR_SHAPE
@@ -138,7 +137,8 @@ def test_blockquant_validation():
     assert _bq(x=None) == ea.ERR_NULL
     assert _bq(s=None) == ea.ERR_NULL
     assert _bq(d=32) == ea.ERR_SHAPE
-    assert _bq(d=256) == ea.ERR_SHAPE
+    assert _bq(d=256, x=None) == ea.ERR_NULL  # d = 256 passes the shape check
+    assert _bq(d=512) == ea.ERR_SHAPE
     assert _bq(br=64) == ea.ERR_VALUE
     assert _bq(br=-1) == ea.ERR_VALUE
     assert _bq(x=P + 2) == ea.ERR_ALIGN
@@ -186,6 +186,7 @@ def test_rope_blockquant_validation():
     assert _rq(inter=2) == ea.ERR_VALUE
     assert _rq(br=64) == ea.ERR_VALUE
     assert _rq(d=96) == ea.ERR_SHAPE
+    assert _rq(d=256, x=None) == ea.ERR_NULL
     assert _rq(c=P + 3 * P2 + 4) == ea.ERR_ALIGN   # tables need 16-byte alignment
     assert _rq(x8=P + 100 * 16) == ea.ERR_VALUE
     assert _rq(N=0) == 0

@@ -41,7 +41,7 @@ def _gpu_quant(x_host, signs, block_rows):
     return c.cpu().numpy(), sc.cpu().numpy()
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("N", [1, 130, 300, 1024])
 @pytest.mark.parametrize("rotate", [True, False])
 @pytest.mark.parametrize("block_rows", [128, 0])
@@ -99,7 +99,7 @@ def _rmse(a, b):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("N", [100, 256, 1000])
 def test_fp8_attention_vs_emulation_full(causal, d, N):
     w = workloads.Workload(f"fp8_n{N}_d{d}", 2, 3, N, d, causal, seed=50 + N, dist="outlier_sd10")
@@ -176,3 +176,44 @@ def test_fp8_lse_vs_exact_normal_inputs():
     mx, rmse = err_stats(o, o_ex)
     print(f"fp8 normal: max={mx:.3e} rmse={rmse:.3e} lse={np.abs(lse - l_ex).max():.3e}")
     assert rmse <= 3e-3 and np.abs(lse - l_ex).max() <= 5e-2
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_d256_full_size_sampled_rows(causal):
+    """Head dim 256 at full size (B2 H8 N8192, the report's 2048-wide model
+    at d = 256): GPU pre-pass and attention, 128 sampled rows in each of three
+    heads against the emulation and exact attention."""
+    w = workloads.Workload("fp8_b2h8n8192d256", 2, 8, 8192, 256, causal, seed=31,
+                           dist="outlier_sd10")
+    say(w.name + ("_causal" if causal else ""))
+    q, k, v = _bf16_host(w)
+    signs = workloads.gen_signs(w.d)
+    ts = torch.from_numpy(signs).to(DEV)
+    tq, tk, tv = (_dev_bf16(x) for x in (q, k, v))
+    q8, sq = ea.blockquant_hadamard(tq, ts, 128)
+    k8, sk = ea.blockquant_hadamard(tk, ts, 128)
+    v8, sv = ea.blockquant_hadamard(tv, None, 128)
+    o, lse = ea.attn_fwd_fp8(q8, k8, v8, sq, sk, sv, causal=causal, softmax_scale=w.softmax_scale)
+    torch.cuda.synchronize()
+    o, lse = to_np(o), lse.cpu().numpy().astype(np.float64)
+    got, ref_ex, ref_em, l_got, l_em = [], [], [], [], []
+    for b, h in ((0, 0), (1, 3), (1, 7)):
+        sl = [x[b:b + 1, :, h:h + 1] for x in (q, k, v)]
+        rows = workloads.sample_rows(1, 1, w.N, 128, seed=91 + h)
+        o_ex, _ = oracle.naive_attention_rows(*sl, w.softmax_scale, causal, rows)
+        o_em, le = oracle.fp8_attention_emulation(*_quant_all(*sl, signs, 128), w.softmax_scale,
+                                                  causal, rows=rows)
+        i = rows[:, 2]
+        got.append(o[b, i, h])
+        l_got.append(lse[b, h, i])
+        ref_ex.append(o_ex)
+        ref_em.append(o_em)
+        l_em.append(le)
+    o, o_ex, o_em = (np.concatenate(a) for a in (got, ref_ex, ref_em))
+    e_kernel, e_em, e_ex = _rmse(o, o_em), _rmse(o_em, o_ex), _rmse(o, o_ex)
+    lerr = float(np.abs(np.concatenate(l_got) - np.concatenate(l_em)).max())
+    print(f"{w.name}: rmse gpu-vs-emulation={e_kernel:.3e} emulation floor={e_em:.3e} "
+          f"gpu-vs-exact={e_ex:.3e} lse={lerr:.3e}", flush=True)
+    assert e_kernel <= 0.1 * e_em
+    assert e_ex <= 3e-2
+    assert lerr <= 1e-3

@@ -104,7 +104,7 @@ def _rmse(a, b):
 
 
 @pytest.mark.parametrize("N,d,H,Hkv,causal", [(300, 128, 6, 2, False), (1000, 64, 4, 1, True),
-                                               (1000, 128, 8, 2, True)])
+                                               (1000, 128, 8, 2, True), (600, 256, 4, 2, True)])
 def test_fp8_gqa_vs_emulation(N, d, H, Hkv, causal):
     tag = f"gqa_fp8_n{N}_d{d}_h{H}kv{Hkv}" + ("_causal" if causal else "")
     say(tag)

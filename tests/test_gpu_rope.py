@@ -37,7 +37,7 @@ def _gpu_rope_quant(x, cos, sin, interleaved, signs, block_rows):
     return c.cpu().numpy(), sc.cpu().numpy()
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("N", [1, 130, 1024])
 @pytest.mark.parametrize("interleaved", [True, False])
 @pytest.mark.parametrize("rotate,block_rows", [(True, 128), (False, 128), (True, 0)])

@@ -91,7 +91,7 @@ def test_encode_matches_torch_cast_fp32():
 
 # ---------------------------------------------------------------- Hadamard
 
-@pytest.mark.parametrize("d", [2, 4, 64, 128])
+@pytest.mark.parametrize("d", [2, 4, 64, 128, 256])
 def test_sylvester_orthogonality(d):
     h = sylvester_hadamard(d)
     assert np.array_equal(h @ h.T, d * np.eye(d))
@@ -99,13 +99,13 @@ def test_sylvester_orthogonality(d):
         assert h.tolist() == [[1, 1], [1, -1]]
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_fwht_equals_dense_product(d):
     x = workloads.gen_random((5, 3, d), 1).astype(np.float64)
     np.testing.assert_allclose(fwht(x), x @ sylvester_hadamard(d), rtol=1e-13, atol=1e-12)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_fwht_fp32_within_rounding_bound(d):
     x = workloads.gen_random((1000, d), 2)
     y32 = fwht(x).astype(np.float64)
@@ -114,7 +114,7 @@ def test_fwht_fp32_within_rounding_bound(d):
     assert np.all(np.abs(y32 - y64) <= bound)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_rotation_preserves_qkt(d):
     """M M^T = I, so (QM)(KM)^T = QK^T (incoherent processing leaves S unchanged)."""
     s = workloads.gen_signs(d, seed=4).astype(np.float64)
