@@ -168,28 +168,26 @@ __device__ __forceinline__ void tile_compute(const char* smem, const uint32_t (&
 #undef TR_PAIR
 }
 
-// NW waves per workgroup (32 query rows each): 8 for long sequences (one
-// workgroup per CU, K/V tiles shared by 256 rows), 4 for short ones (two
-// workgroups per CU, so one's start-up and epilogue overlap the other's tiles).
-template <int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(64 * NW, D > 128 ? 1 : 2) void attn_fwd_bf16_kernel(
-    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    __bf16* __restrict__ O, float* __restrict__ LSE, int H, int Hkv, int N, float scale_log2,
-    int nqb, int xcd_remap) {
-  using G = Geo<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * G::STAGE];
+// One workgroup's work item: query block qblk (32 * NW rows) of head bh,
+// against every visible key.
+// Causal work runs persistent (d <= 128; at d = 256 the loop around the
+// body would push the one-wave-per-SIMD kernel into spilling).
+template <int D, bool CAUSAL>
+constexpr bool persistent() { return CAUSAL && D <= 128; }
 
+template <int D, bool CAUSAL, int NW>
+__device__ __forceinline__ void attend_block(char* smem, const __bf16* __restrict__ Q,
+                                             const __bf16* __restrict__ K,
+                                             const __bf16* __restrict__ V, __bf16* __restrict__ O,
+                                             float* __restrict__ LSE, int H, int Hkv, int N,
+                                             float scale_log2, int bh, int qblk) {
+  using G = Geo<D>;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int li = lane & 31;
   const int hh = lane >> 5;
 
-  int L = blockIdx.x;
-  if (xcd_remap) L = (L & 7) * (gridDim.x >> 3) + (L >> 3);  // one head's q-blocks per XCD
-  const int qb_raw = L % nqb;
-  const int bh = L / nqb;
-  const int qblk = CAUSAL ? (nqb - 1 - qb_raw) : qb_raw;  // heaviest causal blocks first
   const int b = bh / H;
   const int h = bh - b * H;
   const int64_t rs = (int64_t)H * D;
@@ -311,16 +309,94 @@ __global__ __launch_bounds__(64 * NW, D > 128 ? 1 : 2) void attn_fwd_bf16_kernel
   }
 }
 
+// NW waves per workgroup (32 query rows each): 8 for long sequences (one
+// workgroup per CU, K/V tiles shared by 256 rows), 4 for short ones (two
+// workgroups per CU, so one's start-up and epilogue overlap the other's tiles).
+//
+// Non-causal: one workgroup per (b, h, query block).  With xcd_remap, one
+// head's query blocks run on one XCD (its K/V stay in that XCD's L2).
+//
+// Causal, nunits > 0 (persistent, the FlashAttention-3 report's answer to the
+// uneven causal work, section 3): unit u = query blocks nqb-1-p and p
+// (p = u % npair) of head u / npair, whose visible key counts add up to the
+// same for every p, so every unit costs the same.  The grid is one slot per
+// workgroup that fits on the GPU; slot s takes units s, s + gridDim.x, ...
+// (heavier block of a unit first).  With xcd_remap the units of one head stay
+// on one XCD.  Causal, nunits == 0: one workgroup per query block, heaviest
+// first, dispatched by the hardware as CUs free up.
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW, D > 128 ? 1 : 2) void attn_fwd_bf16_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    __bf16* __restrict__ O, float* __restrict__ LSE, int H, int Hkv, int N, float scale_log2,
+    int nqb, int xcd_remap, int nunits) {
+  using G = Geo<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * G::STAGE];
+  if constexpr (!persistent<D, CAUSAL>()) {
+    int L = blockIdx.x;
+    if (xcd_remap) L = (L & 7) * (gridDim.x >> 3) + (L >> 3);
+    const int qb = L % nqb;  // causal: heaviest query blocks first
+    attend_block<D, CAUSAL, NW>(smem, Q, K, V, O, LSE, H, Hkv, N, scale_log2, L / nqb,
+                                CAUSAL ? nqb - 1 - qb : qb);
+  } else {
+    // One call site for both causal modes (a second inlined copy of the
+    // block would not fit the registers).
+    const int npair = (nqb + 1) / 2;
+    const int nslot = nunits > 0 ? nunits : (int)gridDim.x;
+    int s = blockIdx.x, second = 0;  // unit (or block) slot; which block of the unit
+#pragma nounroll
+    while (s < nslot) {
+      const int u = xcd_remap ? (s & 7) * (nslot >> 3) + (s >> 3) : s;
+      int bh, qblk, last = 1;
+      if (nunits > 0) {
+        const int p = u % npair;
+        bh = u / npair;
+        qblk = second ? p : nqb - 1 - p;
+        last = second || p == nqb - 1 - p;
+      } else {
+        bh = u / nqb;
+        qblk = nqb - 1 - u % nqb;
+      }
+      attend_block<D, CAUSAL, NW>(smem, Q, K, V, O, LSE, H, Hkv, N, scale_log2, bh, qblk);
+      if (last) {
+        second = 0;
+        s += gridDim.x;
+      } else {
+        second = 1;
+      }
+      __syncthreads();  // every wave is done with this block's LDS tiles
+    }
+  }
+}
+
 template <int D, bool CAUSAL, int NW>
 hipError_t launch_nw(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                      int Hkv, int N, float scale, hipStream_t stream) {
   constexpr int kBR = 32 * NW;
   const int nqb = (N + kBR - 1) / kBR;
-  const int64_t grid = (int64_t)B * H * nqb;
-  const int remap = (grid % 8 == 0) ? 1 : 0;
+  int64_t grid = (int64_t)B * H * nqb;
+  int64_t nunits = 0;
+  if constexpr (persistent<D, CAUSAL>()) {
+    const int64_t units = (int64_t)B * H * ((nqb + 1) / 2);
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        ncu <= 0)
+      return hipErrorInvalidDevice;
+    const int64_t slots = (int64_t)ncu * (NW == 8 ? 1 : 2);  // resident workgroups per CU
+    // Blocks no more than the CUs: one workgroup each, all at once (a pair
+    // would be the longer path).  Otherwise pairs, if they fill the slots in
+    // whole rounds: with a last round less than 90% full, the hardware's own
+    // dispatch of the single blocks (heaviest first) packs better.
+    const int64_t rounds = (units + slots - 1) / slots;
+    if (grid > ncu && (units <= slots || units * 10 >= rounds * slots * 9)) {
+      nunits = units;
+      grid = units < slots ? units : slots;
+    }
+  }
+  const int remap = (grid % 8 == 0 && (nunits == 0 || nunits % 8 == 0)) ? 1 : 0;
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, NW>), dim3((unsigned)grid), dim3(64 * NW), 0,
                      stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse,
-                     H, Hkv, N, scale * kLog2e, nqb, remap);
+                     H, Hkv, N, scale * kLog2e, nqb, remap, (int)nunits);
   return hipGetLastError();
 }
 

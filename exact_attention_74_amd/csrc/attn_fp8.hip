@@ -113,15 +113,20 @@ __device__ __forceinline__ void mask_s8(f32x16 (&sacc)[4], int k0, int N, bool c
     }
 }
 
+// Causal work runs persistent at d <= 128 (at d = 256 the loop around the
+// body would not fit the registers of the one-wave-per-SIMD kernel).
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(64 * waves<D>(), 1) void attn_fwd_fp8_kernel(
-    const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
-    const float* __restrict__ SQ, const float* __restrict__ SK, const float* __restrict__ SV,
-    __bf16* __restrict__ O, float* __restrict__ LSE, int H, int Hkv, int N, float scale_log2,
-    int nqb, int xcd_remap) {
+constexpr bool persistent8() { return CAUSAL && D <= 128; }
+
+// One workgroup's work item: query block qblk (32 * NW rows) of head bh.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void attend_block8(
+    char* smem, const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
+    const uint8_t* __restrict__ V, const float* __restrict__ SQ, const float* __restrict__ SK,
+    const float* __restrict__ SV, __bf16* __restrict__ O, float* __restrict__ LSE, int H, int Hkv,
+    int N, float scale_log2, int bh, int qblk) {
   using G = Geo8<D>;
   constexpr int kBR = 32 * G::NW;  // query rows per workgroup
-  __shared__ __attribute__((aligned(1024))) char smem[2 * G::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -129,11 +134,6 @@ __global__ __launch_bounds__(64 * waves<D>(), 1) void attn_fwd_fp8_kernel(
   const int li = lane & 31;
   const int hh = lane >> 5;
 
-  int L = blockIdx.x;
-  if (xcd_remap) L = (L & 7) * (gridDim.x >> 3) + (L >> 3);
-  const int qb_raw = L % nqb;
-  const int bh = L / nqb;
-  const int qblk = CAUSAL ? (nqb - 1 - qb_raw) : qb_raw;
   const int b = bh / H;
   const int h = bh - b * H;
   const int64_t rs = (int64_t)H * D;
@@ -351,17 +351,82 @@ _Pragma("unroll")                                                               
   }
 }
 
+// Non-causal (and causal at d = 256): one workgroup per (b, h, query block),
+// causal blocks heaviest first; with xcd_remap one head's blocks run on one
+// XCD.  Causal at d <= 128: as the bf16 kernel, persistent slots over units of
+// two query blocks (nqb-1-p, p) of equal total cost when nunits > 0, one
+// workgroup per block (heaviest first) when nunits == 0.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64 * waves<D>(), 1) void attn_fwd_fp8_kernel(
+    const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
+    const float* __restrict__ SQ, const float* __restrict__ SK, const float* __restrict__ SV,
+    __bf16* __restrict__ O, float* __restrict__ LSE, int H, int Hkv, int N, float scale_log2,
+    int nqb, int xcd_remap, int nunits) {
+  using G = Geo8<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * G::STAGE];
+  if constexpr (!persistent8<D, CAUSAL>()) {
+    int L = blockIdx.x;
+    if (xcd_remap) L = (L & 7) * (gridDim.x >> 3) + (L >> 3);
+    const int qb = L % nqb;
+    attend_block8<D, CAUSAL>(smem, Q, K, V, SQ, SK, SV, O, LSE, H, Hkv, N, scale_log2, L / nqb,
+                             CAUSAL ? nqb - 1 - qb : qb);
+  } else {
+    const int npair = (nqb + 1) / 2;
+    const int nslot = nunits > 0 ? nunits : (int)gridDim.x;
+    int s = blockIdx.x, second = 0;
+#pragma nounroll
+    while (s < nslot) {
+      const int u = xcd_remap ? (s & 7) * (nslot >> 3) + (s >> 3) : s;
+      int bh, qblk, last = 1;
+      if (nunits > 0) {
+        const int p = u % npair;
+        bh = u / npair;
+        qblk = second ? p : nqb - 1 - p;
+        last = second || p == nqb - 1 - p;
+      } else {
+        bh = u / nqb;
+        qblk = nqb - 1 - u % nqb;
+      }
+      attend_block8<D, CAUSAL>(smem, Q, K, V, SQ, SK, SV, O, LSE, H, Hkv, N, scale_log2, bh, qblk);
+      if (last) {
+        second = 0;
+        s += gridDim.x;
+      } else {
+        second = 1;
+      }
+      __syncthreads();  // every wave is done with this block's LDS tiles
+    }
+  }
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch(const void* q8, const void* k8, const void* v8, const float* sq, const float* sk,
                   const float* sv, void* o, float* lse, int B, int H, int Hkv, int N,
                   float scale, hipStream_t stream) {
   constexpr int kBR = 32 * waves<D>();
   const int nqb = (N + kBR - 1) / kBR;
-  const int64_t grid = (int64_t)B * H * nqb;
-  const int remap = (grid % 8 == 0) ? 1 : 0;
+  int64_t grid = (int64_t)B * H * nqb;
+  int64_t nunits = 0;
+  if constexpr (persistent8<D, CAUSAL>()) {
+    const int64_t units = (int64_t)B * H * ((nqb + 1) / 2);
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        ncu <= 0)
+      return hipErrorInvalidDevice;
+    const int64_t slots = ncu;  // one resident workgroup per CU
+    // persistent only with more blocks than CUs and when the equal units
+    // fill the slots in whole rounds (last round at least 90% full)
+    const int64_t rounds = (units + slots - 1) / slots;
+    if (grid > ncu && (units <= slots || units * 10 >= rounds * slots * 9)) {
+      nunits = units;
+      grid = units < slots ? units : slots;
+    }
+  }
+  const int remap = (grid % 8 == 0 && (nunits == 0 || nunits % 8 == 0)) ? 1 : 0;
   hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(64 * waves<D>()), 0,
                      stream, (const uint8_t*)q8, (const uint8_t*)k8, (const uint8_t*)v8, sq, sk, sv,
-                     (__bf16*)o, lse, H, Hkv, N, scale * kLog2e, nqb, remap);
+                     (__bf16*)o, lse, H, Hkv, N, scale * kLog2e, nqb, remap, (int)nunits);
   return hipGetLastError();
 }
 

@@ -147,6 +147,28 @@ def test_sweep_sampled_rows(w):
     _check(rows_of(o, rows)[:, :dl], lse_rows(lse, rows), o_ref, l_ref, w.name, absv)
 
 
+@pytest.mark.parametrize("B,H,N,d", [(2, 16, 5000, 128), (2, 16, 8192, 128), (3, 5, 3000, 128),
+                                     (1, 7, 2500, 64), (4, 16, 4096, 128)])
+def test_causal_schedules_sampled_rows(B, H, N, d):
+    """Causal work runs persistent (workgroup slots take equal-cost pairs of
+    query blocks) when there are more blocks than CUs and the pairs fill the
+    slots in whole rounds, else one workgroup per query block.  Per-block:
+    B2 H16 N5000 (320 pairs on 256 slots) and B1 H7 N2500 d64 (140 blocks);
+    persistent: the others (several rounds, fewer pairs than slots).
+    Sampled rows against the oracle, and a second run bit for bit."""
+    w = workloads.Workload(f"causal_sched_b{B}h{H}n{N}d{d}", B, H, N, d, True, seed=40 + N)
+    say(w.name)
+    host, dev = bf16_inputs(w)
+    o, lse = _run(dev, True, w.softmax_scale)
+    o2, lse2 = _run(dev, True, w.softmax_scale)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+    rows = workloads.sample_rows(B, H, N, 768, seed=N + 1)
+    o_ref, l_ref = oracle.naive_attention_rows(*host, w.softmax_scale, True, rows)
+    absv, _ = oracle.naive_attention_rows(host[0], host[1], np.abs(host[2]), w.softmax_scale,
+                                          True, rows)
+    _check(rows_of(o, rows), lse_rows(lse, rows), o_ref, l_ref, w.name, absv)
+
+
 def test_causal_row0_equals_v0_bitwise():
     w = workloads.Workload("row0", 2, 4, 300, 128, True, seed=31)
     say(w.name)

@@ -19,7 +19,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_helpers import DEV, err_stats, say, to_np
+from gpu_helpers import DEV, err_stats, rows_of, say, to_np
 
 import exact_attention_74_amd as ea
 
@@ -216,4 +216,33 @@ def test_fp8_d256_full_size_sampled_rows(causal):
           f"gpu-vs-exact={e_ex:.3e} lse={lerr:.3e}", flush=True)
     assert e_kernel <= 0.1 * e_em
     assert e_ex <= 3e-2
+    assert lerr <= 1e-3
+
+
+@pytest.mark.parametrize("B,H,N,d", [(2, 16, 5000, 128), (3, 5, 3000, 64), (2, 8, 8192, 128),
+                                     (4, 16, 4096, 128)])
+def test_fp8_causal_schedules_sampled_rows(B, H, N, d):
+    """Causal FP8 work in both schedules.  One workgroup per query block:
+    B2 H16 N5000 (its 320 equal-cost block pairs would leave the second round
+    of 256 slots a quarter full) and B3 H5 N3000 d64 (180 blocks, fewer than
+    the CUs).  Persistent slots over block pairs: B2 H8 N8192 (one round) and
+    B4 H16 N4096 (two).  Sampled rows against the emulation, and a second run
+    bit for bit."""
+    w = workloads.Workload(f"fp8_causal_sched_b{B}h{H}n{N}d{d}", B, H, N, d, True, seed=70 + N,
+                           dist="outlier_sd10")
+    say(w.name)
+    q, k, v = _bf16_host(w)
+    qs = _quant_all(q, k, v, workloads.gen_signs(d), 128)
+    o, lse = _gpu_fp8(*qs, w.softmax_scale, True)
+    o2, lse2 = _gpu_fp8(*qs, w.softmax_scale, True)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+    rows = workloads.sample_rows(B, H, N, 384, seed=N + 3)
+    o_em, l_em = oracle.fp8_attention_emulation(*qs, w.softmax_scale, True, rows=rows)
+    o_ex, _ = oracle.naive_attention_rows(q, k, v, w.softmax_scale, True, rows)
+    got = rows_of(o, rows)
+    e_kernel, e_scheme = _rmse(got, o_em), _rmse(o_em, o_ex)
+    lerr = float(np.abs(lse[rows[:, 0], rows[:, 1], rows[:, 2]] - l_em).max())
+    print(f"{w.name}: rmse(gpu-emul)={e_kernel:.3e} rmse(emul-exact)={e_scheme:.3e} "
+          f"lse={lerr:.3e}", flush=True)
+    assert e_kernel <= 0.1 * e_scheme
     assert lerr <= 1e-3
