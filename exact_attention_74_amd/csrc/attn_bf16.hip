@@ -316,8 +316,8 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
 // Non-causal: one workgroup per (b, h, query block).  With xcd_remap, one
 // head's query blocks run on one XCD (its K/V stay in that XCD's L2).
 //
-// Causal, nunits > 0 (persistent, the FlashAttention-3 report's answer to the
-// uneven causal work, section 3): unit u = query blocks nqb-1-p and p
+// Causal, nunits > 0 (a persistent, resident kernel: FlashAttention-3 report,
+// section 5.1): unit u = query blocks nqb-1-p and p
 // (p = u % npair) of head u / npair, whose visible key counts add up to the
 // same for every p, so every unit costs the same.  The grid is one slot per
 // workgroup that fits on the GPU; slot s takes units s, s + gridDim.x, ...

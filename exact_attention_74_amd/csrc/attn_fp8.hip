@@ -355,7 +355,9 @@ _Pragma("unroll")                                                               
 // causal blocks heaviest first; with xcd_remap one head's blocks run on one
 // XCD.  Causal at d <= 128: as the bf16 kernel, persistent slots over units of
 // two query blocks (nqb-1-p, p) of equal total cost when nunits > 0, one
-// workgroup per block (heaviest first) when nunits == 0.
+// workgroup per block (heaviest first) when nunits == 0.  (The report's
+// section 5.1 lists the persistent kernel as not yet joined with its FP8
+// kernel; here both forwards share the schedule.)
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * waves<D>(), 1) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
