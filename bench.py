@@ -52,6 +52,10 @@ def parse():
     p.add_argument("--rope-reps", type=int, default=20,
                    help="timed launches of the RoPE-fused pre-pass on the fp8 workload's Q; 0 "
                         "skips them")
+    p.add_argument("--causal-reps", type=int, default=20,
+                   help="launches of the causal forwards on the same workloads (0: skip)")
+    p.add_argument("--d256-reps", type=int, default=20,
+                   help="launches of the head-dim-256 forwards, B2 H8 N8192 (0: skip)")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run one plain 256 MiB device copy (untimed), the reference that "
                         "scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -112,6 +116,23 @@ def cpu_baseline(w, target_s: float):
         "host_cpus": os.cpu_count(),
         "affinity_cpus": len(os.sched_getaffinity(0)),
     }
+
+
+def time_reps(fn, reps: int, stream) -> float:
+    """Median seconds of ``reps`` launches of ``fn``, each bracketed by HIP
+    events on ``stream``, after three untimed ones."""
+    import numpy as np
+    import torch
+    for _ in range(3):
+        fn()
+    ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+          for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e-3
 
 
 def main():
@@ -256,17 +277,7 @@ def main():
         def bwd():
             ea.attn_bwd_bf16(q, k, v, o16, lse16, do, causal=a.causal, softmax_scale=scale,
                              dq=dq, dk=dk, dv=dv, workspace=ws)
-        for _ in range(3):
-            bwd()
-        bev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-               for _ in range(a.bwd_reps)]
-        for e0, e1 in bev:
-            e0.record(stream)
-            bwd()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        tb = [e0.elapsed_time(e1) for e0, e1 in bev]
-        t_bwd = float(np.median(tb)) * 1e-3
+        t_bwd = time_reps(bwd, a.bwd_reps, stream)
         bflops = 2.5 * w16.flops()  # five N^2 d products against the forward's two
         out["backward"] = {
             "kernel": "attn_bwd_bf16 (prep + dK/dV + dQ kernels)", "workload": w16.name,
@@ -285,22 +296,63 @@ def main():
         def rq():
             ea.rope_blockquant_hadamard(q8in, rc, rsn, False, signs, 128, out=codes[0],
                                         scale=scales[0])
-        for _ in range(3):
-            rq()
-        rev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-               for _ in range(a.rope_reps)]
-        for e0, e1 in rev:
-            e0.record(stream)
-            rq()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        t_rq = float(np.median([e0.elapsed_time(e1) for e0, e1 in rev])) * 1e-3
+        t_rq = time_reps(rq, a.rope_reps, stream)
         rq_bytes = bq_bytes + 2 * N * (d // 2) * 4
         out["rope_blockquant_hadamard"] = {
             "workload": f"{w8.name} (Q), half-split RoPE", "gbps": round(rq_bytes / t_rq / 1e9, 1),
             "pct_of_hbm_peak": round(100 * rq_bytes / t_rq / 1e9 / PEAK_HBM_GBS, 2),
             "bytes_per_launch": rq_bytes, "us": round(t_rq * 1e6, 2),
             "vs_plain_prepass_us": round(t_bq * 1e6, 2)}
+    if a.causal_reps > 0 and not a.causal:
+        # The same two workloads with the causal mask (visible key pairs only:
+        # 2 B H N^2 d flop); causal work at d <= 128 runs on persistent slots
+        # over equal-cost pairs of query blocks.
+        print(f"[bench] causal forwards: {a.causal_reps} launches each", file=sys.stderr,
+              flush=True)
+        t_c16 = time_reps(lambda: ea.attn_fwd_bf16(q, k, v, causal=True, softmax_scale=scale,
+                                                   out=o16, lse=lse16), a.causal_reps, stream)
+        t_c8 = time_reps(lambda: ea.attn_fwd_fp8(codes[0], codes[1], codes[2], *scales,
+                                                 causal=True, softmax_scale=scale, out=o8,
+                                                 lse=lse8), a.causal_reps, stream)
+        f16, f8 = w16.flops() / 2, w8.flops() / 2
+        out["causal"] = {
+            "flops_counted": "2 B H N^2 d (visible pairs)", "timing": "median of per-call HIP event times",
+            "attn_fwd_bf16": {"workload": w16.name + "_causal", "value": round(f16 / t_c16 / 1e12, 2),
+                              "pct_of_peak": round(100 * f16 / t_c16 / 1e12 / PEAK_BF16_TFLOPS, 2),
+                              "ms": round(t_c16 * 1e3, 4)},
+            "attn_fwd_fp8": {"workload": w8.name + "_causal", "value": round(f8 / t_c8 / 1e12, 2),
+                             "pct_of_peak": round(100 * f8 / t_c8 / 1e12 / PEAK_FP8_TFLOPS, 2),
+                             "ms": round(t_c8 * 1e3, 4)},
+            "finite": bool(torch.isfinite(o16).all().item() and torch.isfinite(o8).all().item())}
+    if a.d256_reps > 0:
+        # Head dim 256 (the report's best FP8 case), B2 H8 N8192: the 2048-wide
+        # model at d = 256.  FP8 codes from the pre-pass (untimed here).
+        print(f"[bench] d=256 forwards: {a.d256_reps} launches each", file=sys.stderr, flush=True)
+        w256 = workloads.Workload("attn_fwd_b2h8n8192d256_outlier30", 2, 8, 8192, 256, False,
+                                  seed=4, dist="outlier30")
+        x256 = [dev_bf16(x) for x in workloads.gen_qkv(w256)]
+        s256 = torch.from_numpy(workloads.gen_signs(256)).to(dev)
+        q2, sq2 = ea.blockquant_hadamard(x256[0], s256, 128)
+        k2, sk2 = ea.blockquant_hadamard(x256[1], s256, 128)
+        v2, sv2 = ea.blockquant_hadamard(x256[2], None, 128)
+        o2 = torch.empty_like(x256[0])
+        l2 = torch.empty((2, 8, 8192), dtype=torch.float32, device=dev)
+        sc2 = w256.softmax_scale
+        t_a16 = time_reps(lambda: ea.attn_fwd_bf16(*x256, softmax_scale=sc2, out=o2, lse=l2),
+                          a.d256_reps, stream)
+        t_a8 = time_reps(lambda: ea.attn_fwd_fp8(q2, k2, v2, sq2, sk2, sv2, softmax_scale=sc2,
+                                                 out=o2, lse=l2), a.d256_reps, stream)
+        f = w256.flops()
+        out["d256"] = {
+            "workload": w256.name, "timing": "median of per-call HIP event times",
+            "attn_fwd_fp8": {"value": round(f / t_a8 / 1e12, 2),
+                             "pct_of_peak": round(100 * f / t_a8 / 1e12 / PEAK_FP8_TFLOPS, 2),
+                             "ms": round(t_a8 * 1e3, 4)},
+            "attn_fwd_bf16": {"value": round(f / t_a16 / 1e12, 2),
+                              "pct_of_peak": round(100 * f / t_a16 / 1e12 / PEAK_BF16_TFLOPS, 2),
+                              "ms": round(t_a16 * 1e3, 4)},
+            "finite": bool(torch.isfinite(o2).all().item())}
+        del x256, q2, k2, v2, o2, l2
     if not a.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w16, a.cpu_seconds)
