@@ -8,7 +8,10 @@
 // workgroup's start-up and epilogue overlap the other's key tiles).  The
 // key/value sequence is streamed in blocks of 64 keys with the online-softmax
 // recurrence of the FlashAttention-3 report, section 3 (running max m,
-// running sum l, one final normalisation).
+// running sum l, one final normalisation).  Causal work at d <= 128 runs on
+// persistent workgroup slots over pairs of query blocks of equal total cost
+// (see the kernel below).  Head dim 256 runs 4-wave workgroups, one wave
+// per SIMD.
 //
 // Transposed formulation.  Each wave computes S^T = K Q^T (keys as MFMA rows,
 // its 32 queries as MFMA columns), so the accumulator keeps every query on one

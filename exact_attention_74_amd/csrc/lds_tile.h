@@ -98,7 +98,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 // that no use of them is scheduled before the wait.
 template <int NE>
 __device__ __forceinline__ void lds_wait_v(bf16x8 (&vf)[4][NE]) {
-  static_assert(NE == 4 || NE == 2, "d = 128 or 64");
+  static_assert(NE == 4 || NE == 2, "four or two 32-dim blocks");
   if constexpr (NE == 4)
     asm volatile("s_waitcnt lgkmcnt(0)"
                  : "+v"(vf[0][0]), "+v"(vf[0][1]), "+v"(vf[0][2]), "+v"(vf[0][3]),
