@@ -380,11 +380,8 @@ hipError_t launch_nw(const void* q, const void* k, const void* v, void* o, float
   int64_t nunits = 0;
   if constexpr (persistent<D, CAUSAL>()) {
     const int64_t units = (int64_t)B * H * ((nqb + 1) / 2);
-    int dev = 0, ncu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        ncu <= 0)
-      return hipErrorInvalidDevice;
+    const int ncu = current_cu_count();
+    if (ncu <= 0) return hipErrorInvalidDevice;
     const int64_t slots = (int64_t)ncu * (NW == 8 ? 1 : 2);  // resident workgroups per CU
     // Blocks no more than the CUs: one workgroup each, all at once (a pair
     // would be the longer path).  Otherwise pairs, if they fill the slots in

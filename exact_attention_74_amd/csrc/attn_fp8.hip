@@ -411,11 +411,8 @@ hipError_t launch(const void* q8, const void* k8, const void* v8, const float* s
   int64_t nunits = 0;
   if constexpr (persistent8<D, CAUSAL>()) {
     const int64_t units = (int64_t)B * H * ((nqb + 1) / 2);
-    int dev = 0, ncu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        ncu <= 0)
-      return hipErrorInvalidDevice;
+    const int ncu = current_cu_count();
+    if (ncu <= 0) return hipErrorInvalidDevice;
     const int64_t slots = ncu;  // one resident workgroup per CU
     // persistent only with more blocks than CUs and when the equal units
     // fill the slots in whole rounds (last round at least 90% full)

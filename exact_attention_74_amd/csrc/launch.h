@@ -5,7 +5,27 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 namespace exattn {
+
+// Compute units of the current device, queried once per device and cached
+// (thread-safe); 0 when the query fails.
+inline int current_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int ncu = 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      ncu <= 0)
+    return 0;
+  if (dev < 64) cache[dev].store(ncu, std::memory_order_relaxed);
+  return ncu;
+}
 
 // Hkv: K/V heads (H a multiple of it); query head h reads K/V head h / (H / Hkv).
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
