@@ -325,8 +325,10 @@ __global__ __launch_bounds__(64 * kNWb, 2) void bwd_dq_kernel(
 // ---------------------------------------------------------------------------
 // dK, dV.  LDS: [2 stages x (LSE*log2e[64], D[64])] then 2 stages x (Q tile,
 // dO tile), both tiles swz_b (read row-wise and transposed).
+// Two waves per SIMD where the kernel fits 256 registers without spilling
+// (d = 64, causal: 246); elsewhere one, with up to 512.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(64 * kNWb, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(64 * kNWb, (D == 64 && CAUSAL) ? 2 : 1) void bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Drow,
     __bf16* __restrict__ dK, __bf16* __restrict__ dV, int H, int Hkv, int N, float scale_log2,
