@@ -411,9 +411,11 @@ hipError_t launch(const void* q8, const void* k8, const void* v8, const float* s
   int64_t nunits = 0;
   if constexpr (persistent8<D, CAUSAL>()) {
     const int64_t units = (int64_t)B * H * ((nqb + 1) / 2);
+    static std::atomic<int> resident{0};
     const int ncu = current_cu_count();
-    if (ncu <= 0) return hipErrorInvalidDevice;
-    const int64_t slots = ncu;  // one resident workgroup per CU
+    const int per_cu = resident_per_cu(attn_fwd_fp8_kernel<D, CAUSAL>, 64 * waves<D>(), resident);
+    if (ncu <= 0 || per_cu <= 0) return hipErrorInvalidDevice;
+    const int64_t slots = (int64_t)ncu * per_cu;  // resident workgroups
     // persistent only with more blocks than CUs and when the equal units
     // fill the slots in whole rounds (last round at least 90% full)
     const int64_t rounds = (units + slots - 1) / slots;

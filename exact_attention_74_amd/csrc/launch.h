@@ -27,6 +27,21 @@ inline int current_cu_count() {
   return ncu;
 }
 
+// Workgroups of `kernel` (block size `threads`, no dynamic LDS) resident on
+// one CU at a time, from the runtime's occupancy calculator; queried once per
+// kernel (the cache slot is the caller's, one per kernel instance) and 0 when
+// the query fails.
+template <typename K>
+inline int resident_per_cu(K kernel, int threads, std::atomic<int>& cache) {
+  const int c = cache.load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n <= 0)
+    return 0;
+  cache.store(n, std::memory_order_relaxed);
+  return n;
+}
+
 // Hkv: K/V heads (H a multiple of it); query head h reads K/V head h / (H / Hkv).
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                                 int B, int H, int Hkv, int N, int d, bool causal,
