@@ -44,19 +44,6 @@ constexpr int kRowsB = 32 * kNWb;  // query rows (dQ) or key rows (dK, dV) per w
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Waits for every outstanding LDS read of this wave, passing the fragments
-// through so that no use of them is scheduled before the wait.
-template <int NF>
-__device__ __forceinline__ void lds_wait_frags(bf16x8 (&f)[NF]) {
-  static_assert(NF == 4 || NF == 8, "d = 64 or 128");
-  if constexpr (NF == 8)
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]),
-                   "+v"(f[6]), "+v"(f[7]));
-  else
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]));
-}
-
 __device__ __forceinline__ void lds_wait_f4(f32x4 (&a)[4], f32x4 (&b)[4]) {
   asm volatile("s_waitcnt lgkmcnt(0)"
                : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]),
@@ -93,15 +80,34 @@ __device__ __forceinline__ void read_tr_frags(const uint32_t (&taddr)[D / 32],
   }
 }
 
+// S-type product over the NF fragments of a group of row reads just issued
+// (one ds_read_b128 each, in order t = 0 .. NF-1): each MFMA waits only for
+// its own fragment, since LDS reads complete in issue order.
+template <int NF>
+__device__ __forceinline__ f32x16 mfma_rows_counted(bf16x8 (&f)[NF], const bf16x8 (&b)[NF]) {
+  f32x16 acc = {};
+  static_for<NF>([&](auto T) __attribute__((always_inline)) {
+    constexpr int t = decltype(T)::value;
+    wait_lds<NF - 1 - t>(f[t]);
+    acc = mfma_bf16(f[t], b[t], acc);
+  });
+  return acc;
+}
+
+// acc[e] += frag[T][e] x b[T] (T = 0, 1) for the fragments read_tr_frags has
+// just issued (two reads per (T, e), e-major), each MFMA waiting only for its
+// own two reads; per accumulator the order stays T = 0, 1.
 template <int NE>
-__device__ __forceinline__ void lds_wait_tr(bf16x8 (&f)[2][NE]) {
-  static_assert(NE == 4 || NE == 2, "d = 128 or 64");
-  if constexpr (NE == 4)
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(f[0][0]), "+v"(f[0][1]), "+v"(f[0][2]), "+v"(f[0][3]), "+v"(f[1][0]),
-                   "+v"(f[1][1]), "+v"(f[1][2]), "+v"(f[1][3]));
-  else
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[0][0]), "+v"(f[0][1]), "+v"(f[1][0]), "+v"(f[1][1]));
+__device__ __forceinline__ void mfma_tr_counted(bf16x8 (&frag)[2][NE], const bf16x8 (&b)[2],
+                                                f32x16 (&acc)[NE]) {
+  static_for<NE>([&](auto E) __attribute__((always_inline)) {
+    constexpr int e = decltype(E)::value;
+    static_for<2>([&](auto TT) __attribute__((always_inline)) {
+      constexpr int T = decltype(TT)::value;
+      wait_lds<4 * NE - 2 - (4 * e + 2 * T)>(frag[T][e]);
+      acc[e] = mfma_bf16(frag[T][e], b[T], acc[e]);
+    });
+  });
 }
 
 // LDS address of this lane's transposed-read source in a tile at LDS byte
@@ -264,18 +270,12 @@ __global__ __launch_bounds__(64 * kNWb, 2) void bwd_dq_kernel(
         constexpr int t = decltype(T)::value;
         f[t] = read_b128<ST * G::STAGE + jh * 32 * G::RB>(ka0 ^ (uint32_t)(32 * t));
       });
-      lds_wait_frags<NF>(f);
-      f32x16 sacc = {};
-#pragma unroll
-      for (int t = 0; t < NF; ++t) sacc = mfma_bf16(f[t], qf[t], sacc);
+      const f32x16 sacc = mfma_rows_counted<NF>(f, qf);
       static_for<NF>([&](auto T) __attribute__((always_inline)) {
         constexpr int t = decltype(T)::value;
         f[t] = read_b128<ST * G::STAGE + jh * 32 * G::RB>(va0 ^ (uint32_t)(32 * t));
       });
-      lds_wait_frags<NF>(f);
-      f32x16 dpacc = {};
-#pragma unroll
-      for (int t = 0; t < NF; ++t) dpacc = mfma_bf16(f[t], gf[t], dpacc);
+      const f32x16 dpacc = mfma_rows_counted<NF>(f, gf);
       bf16x8 ktf[2][NE];
       read_tr_frags<D, ST * G::STAGE, jh>(taddr, ktf);
       // P^T and dS^T; element v holds key k0 + 32 jh + 8 (v / 4) + 4 h + v % 4.
@@ -289,11 +289,7 @@ __global__ __launch_bounds__(64 * kNWb, 2) void bwd_dq_kernel(
         }
         dsb[v >> 3][v & 7] = (__bf16)(p * (dpacc[v] - dd));
       }
-      lds_wait_tr<NE>(ktf);
-#pragma unroll
-      for (int T = 0; T < 2; ++T)
-#pragma unroll
-        for (int e = 0; e < NE; ++e) dqacc[e] = mfma_bf16(ktf[T][e], dsb[T], dqacc[e]);
+      mfma_tr_counted<NE>(ktf, dsb, dqacc);
     });
   };
 
@@ -421,18 +417,12 @@ __global__ __launch_bounds__(64 * kNWb, (D == 64 && CAUSAL) ? 2 : 1) void bwd_dk
         constexpr int t = decltype(T)::value;
         f[t] = read_b128<ST * G::STAGE + jq * 32 * G::RB>(qa0 ^ (uint32_t)(32 * t));
       });
-      lds_wait_frags<NF>(f);
-      f32x16 sacc = {};
-#pragma unroll
-      for (int t = 0; t < NF; ++t) sacc = mfma_bf16(f[t], kt[t], sacc);
+      const f32x16 sacc = mfma_rows_counted<NF>(f, kt);
       static_for<NF>([&](auto T) __attribute__((always_inline)) {
         constexpr int t = decltype(T)::value;
         f[t] = read_b128<ST * G::STAGE + G::TILE + jq * 32 * G::RB>(qa0 ^ (uint32_t)(32 * t));
       });
-      lds_wait_frags<NF>(f);
-      f32x16 dpacc = {};
-#pragma unroll
-      for (int t = 0; t < NF; ++t) dpacc = mfma_bf16(f[t], vt[t], dpacc);
+      const f32x16 dpacc = mfma_rows_counted<NF>(f, vt);
       // LSE*log2e and D of this lane's 16 query rows 32 jq + 8 g + 4 h + (0..3).
       f32x4 l4[4], d4[4];
       static_for<4>([&](auto Gi) __attribute__((always_inline)) {
@@ -454,17 +444,9 @@ __global__ __launch_bounds__(64 * kNWb, (D == 64 && CAUSAL) ? 2 : 1) void bwd_dk
       }
       bf16x8 tf[2][NE];
       read_tr_frags<D, ST * G::STAGE + G::TILE, jq>(taddr, tf);  // dO^T
-      lds_wait_tr<NE>(tf);
-#pragma unroll
-      for (int T = 0; T < 2; ++T)
-#pragma unroll
-        for (int e = 0; e < NE; ++e) dvacc[e] = mfma_bf16(tf[T][e], pb[T], dvacc[e]);
+      mfma_tr_counted<NE>(tf, pb, dvacc);
       read_tr_frags<D, ST * G::STAGE, jq>(taddr, tf);  // Q^T
-      lds_wait_tr<NE>(tf);
-#pragma unroll
-      for (int T = 0; T < 2; ++T)
-#pragma unroll
-        for (int e = 0; e < NE; ++e) dkacc[e] = mfma_bf16(tf[T][e], dsb[T], dkacc[e]);
+      mfma_tr_counted<NE>(tf, dsb, dkacc);
     });
   };
 
