@@ -113,6 +113,28 @@ __device__ __forceinline__ void mask_s8(f32x16 (&sacc)[4], int k0, int N, bool c
     }
 }
 
+// V^T operands of stage ST for NE 32-dim blocks, whose read addresses start
+// at vaddr (eight transposed reads per block; valid after lds_wait_v).
+template <int D, int ST, int NE>
+__device__ __forceinline__ void read_vt(const uint32_t* vaddr, i32x8 (&vf)[2][NE]) {
+  using G = Geo8<D>;
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+    const uint32_t va = vaddr[e];
+    i32x2 r[8];
+    r[0] = read_tr8<G::voff(ST) + 0 * G::RB>(va);
+    r[1] = read_tr8<G::voff(ST) + 16 * G::RB>(va);
+    r[2] = read_tr8<G::voff(ST) + 32 * G::RB>(va);
+    r[3] = read_tr8<G::voff(ST) + 48 * G::RB>(va);
+    r[4] = read_tr8<G::voff(ST) + 64 * G::RB>(va);
+    r[5] = read_tr8<G::voff(ST) + 80 * G::RB>(va);
+    r[6] = read_tr8<G::voff(ST) + 96 * G::RB>(va);
+    r[7] = read_tr8<G::voff(ST) + 112 * G::RB>(va);
+    vf[0][e] = i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
+    vf[1][e] = i32x8{r[4][0], r[4][1], r[5][0], r[5][1], r[6][0], r[6][1], r[7][0], r[7][1]};
+  }
+}
+
 // Causal work runs persistent at d <= 128 (at d = 256 the loop around the
 // body would not fit the registers of the one-wave-per-SIMD kernel).
 template <int D, bool CAUSAL>
@@ -241,6 +263,10 @@ _Pragma("unroll")                                                               
 _Pragma("unroll")                                                                                    \
       for (int j = 0; j < 4; ++j) sacc[j] = mfma_fp8(kf[j][t], qf[t], sacc[j]);                      \
                                                                                                      \
+    /* d <= 128, non-causal: the V^T operands are read now, so that the softmax     */           \
+    /* covers their latency (in the causal kernel they would not fit the registers) */           \
+    i32x8 vf0[2][NEH];                                                                               \
+    if constexpr (NHALF == 1 && !CAUSAL) read_vt<D, ST, NEH>(vaddr, vf0);                            \
     if (MASKED) mask_s8(sacc, k0, N, CAUSAL, qi, hh);                                                \
                                                                                                      \
     const float c_tile = scale_log2 * sq * sk_bh[kb];                                                \
@@ -275,7 +301,8 @@ _Pragma("unroll")                                                               
         pf[u][w] = (int)pack_fp8x4(p[0], p[1], p[2], p[3]);                                          \
       }                                                                                              \
     l = l * alpha + ((rs4[0] + rs4[1]) + (rs4[2] + rs4[3]));                                         \
-    const float f = alpha * (sv_prev / sv);                                                          \
+    /* hardware reciprocal (1 ulp): the ratio only rescales the fp32 accumulator */                \
+    const float f = alpha * (sv_prev * __builtin_amdgcn_rcpf(sv));                                   \
     sv_prev = sv;                                                                                    \
 _Pragma("unroll")                                                                                    \
     for (int e = 0; e < D / 32; ++e) oacc[e] *= f;                                                   \
@@ -284,20 +311,11 @@ _Pragma("unroll")                                                               
 _Pragma("unroll")                                                                                    \
     for (int hf = 0; hf < NHALF; ++hf) {                                                             \
       i32x8 vf[2][NEH];                                                                              \
+      if constexpr (NHALF == 1 && !CAUSAL) {                                                         \
 _Pragma("unroll")                                                                                    \
-      for (int e = 0; e < NEH; ++e) {                                                                \
-        const uint32_t va = vaddr[hf * NEH + e];                                                     \
-        i32x2 r[8];                                                                                  \
-        r[0] = read_tr8<G::voff(ST) + 0 * G::RB>(va);                                                \
-        r[1] = read_tr8<G::voff(ST) + 16 * G::RB>(va);                                               \
-        r[2] = read_tr8<G::voff(ST) + 32 * G::RB>(va);                                               \
-        r[3] = read_tr8<G::voff(ST) + 48 * G::RB>(va);                                               \
-        r[4] = read_tr8<G::voff(ST) + 64 * G::RB>(va);                                               \
-        r[5] = read_tr8<G::voff(ST) + 80 * G::RB>(va);                                               \
-        r[6] = read_tr8<G::voff(ST) + 96 * G::RB>(va);                                               \
-        r[7] = read_tr8<G::voff(ST) + 112 * G::RB>(va);                                              \
-        vf[0][e] = i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};    \
-        vf[1][e] = i32x8{r[4][0], r[4][1], r[5][0], r[5][1], r[6][0], r[6][1], r[7][0], r[7][1]};    \
+        for (int e = 0; e < NEH; ++e) { vf[0][e] = vf0[0][e]; vf[1][e] = vf0[1][e]; }                \
+      } else {                                                                                       \
+        read_vt<D, ST, NEH>(vaddr + hf * NEH, vf);                                                   \
       }                                                                                              \
       lds_wait_v(vf);                                                                                \
                                                                                                      \
