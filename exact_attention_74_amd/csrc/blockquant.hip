@@ -68,11 +68,15 @@ __global__ __launch_bounds__(kThreads) void blockquant_kernel(const __bf16* __re
   const int tid = threadIdx.x;
   const int lr = tid % LPR;
   const int rsub = tid / LPR;
-  const int bid = blockIdx.x;
-  const int sb = bid % nsb;
-  const int bh = bid / nsb;
-  const int b = bh / H;
-  const int h = bh - b * H;
+  // Workgroups run heads fastest: neighbouring workgroups take the same 128
+  // rows of neighbouring heads, which sit side by side in each BSHD row, so
+  // the workgroups in flight read (and write) long contiguous runs.
+  const int h = blockIdx.x % H;
+  const int bsb = blockIdx.x / H;
+  const int sb = bsb % nsb;
+  const int b = bsb / nsb;
+  const int bh = b * H + h;
+  const int bid = bh * nsb + sb;  // scale slot [b, h, sb]
   const int64_t rs = (int64_t)H * D;
   const int64_t head_off = ((int64_t)b * N * H + h) * D;
 
