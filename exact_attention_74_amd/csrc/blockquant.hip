@@ -68,13 +68,23 @@ __global__ __launch_bounds__(kThreads) void blockquant_kernel(const __bf16* __re
   const int tid = threadIdx.x;
   const int lr = tid % LPR;
   const int rsub = tid / LPR;
-  // Workgroups run heads fastest: neighbouring workgroups take the same 128
-  // rows of neighbouring heads, which sit side by side in each BSHD row, so
-  // the workgroups in flight read (and write) long contiguous runs.
-  const int h = blockIdx.x % H;
-  const int bsb = blockIdx.x / H;
-  const int sb = bsb % nsb;
-  const int b = bsb / nsb;
+  // Without RoPE, workgroups run heads fastest: neighbouring workgroups take
+  // the same 128 rows of neighbouring heads, which sit side by side in each
+  // BSHD row, so the workgroups in flight read (and write) long contiguous
+  // runs.  With RoPE, row blocks run fastest (measured faster there: the
+  // workgroups in flight then read different rows of the cos/sin tables).
+  int h, sb, b;
+  if constexpr (ROPE == 0) {
+    h = blockIdx.x % H;
+    const int bsb = blockIdx.x / H;
+    sb = bsb % nsb;
+    b = bsb / nsb;
+  } else {
+    sb = blockIdx.x % nsb;
+    const int bh0 = blockIdx.x / nsb;
+    b = bh0 / H;
+    h = bh0 - b * H;
+  }
   const int bh = b * H + h;
   const int bid = bh * nsb + sb;  // scale slot [b, h, sb]
   const int64_t rs = (int64_t)H * D;
