@@ -307,23 +307,26 @@ _Pragma("unroll")                                                               
 _Pragma("unroll")                                                                                    \
     for (int e = 0; e < D / 32; ++e) oacc[e] *= f;                                                   \
                                                                                                      \
-    /* V^T operands in halves of at most four 32-dim blocks (d = 256: two) */                      \
-_Pragma("unroll")                                                                                    \
-    for (int hf = 0; hf < NHALF; ++hf) {                                                             \
-      i32x8 vf[2][NEH];                                                                              \
-      if constexpr (NHALF == 1 && !CAUSAL) {                                                         \
-_Pragma("unroll")                                                                                    \
-        for (int e = 0; e < NEH; ++e) { vf[0][e] = vf0[0][e]; vf[1][e] = vf0[1][e]; }                \
-      } else {                                                                                       \
-        read_vt<D, ST, NEH>(vaddr + hf * NEH, vf);                                                   \
-      }                                                                                              \
-      lds_wait_v(vf);                                                                                \
-                                                                                                     \
+    if constexpr (NHALF == 1 && !CAUSAL) {                                                           \
+      /* the early reads: waited for in place (no copy of a register in flight) */                 \
+      lds_wait_v(vf0);                                                                               \
 _Pragma("unroll")                                                                                    \
       for (int u = 0; u < 2; ++u)                                                                    \
 _Pragma("unroll")                                                                                    \
-        for (int e = 0; e < NEH; ++e)                                                                \
-          oacc[hf * NEH + e] = mfma_fp8(vf[u][e], pf[u], oacc[hf * NEH + e]);                        \
+        for (int e = 0; e < NEH; ++e) oacc[e] = mfma_fp8(vf0[u][e], pf[u], oacc[e]);                 \
+    } else {                                                                                         \
+      /* V^T operands in halves of at most four 32-dim blocks (d = 256: two) */                    \
+_Pragma("unroll")                                                                                    \
+      for (int hf = 0; hf < NHALF; ++hf) {                                                           \
+        i32x8 vf[2][NEH];                                                                            \
+        read_vt<D, ST, NEH>(vaddr + hf * NEH, vf);                                                   \
+        lds_wait_v(vf);                                                                              \
+_Pragma("unroll")                                                                                    \
+        for (int u = 0; u < 2; ++u)                                                                  \
+_Pragma("unroll")                                                                                    \
+          for (int e = 0; e < NEH; ++e)                                                              \
+            oacc[hf * NEH + e] = mfma_fp8(vf[u][e], pf[u], oacc[hf * NEH + e]);                      \
+      }                                                                                              \
     }                                                                                                \
 
 #define STEP8(ST, KB, MASKED)                                                                        \
