@@ -12,7 +12,11 @@ Each launch is bracketed by HIP events on the stream it runs on; the printed
 ``value`` is the bf16 attention TFLOP/s (4*B*H*N^2*d per launch over its
 median event time), with the fp8 figure and the pre-pass GB/s beside it.
 
-Prints ONE JSON line (see the repository's design notes for every field).
+After the timed steps, further legs are timed the same way, each on its own
+launches: the bf16 gradients, the RoPE-fused pre-pass, the causal forwards,
+the head-dim-256 forwards and the bf16 forward on B2 H32 N4096, and (unless
+--no-cpu-baseline) the fp64 CPU oracle on a bounded sample of the bf16
+workload.  Prints ONE JSON line.
 """
 from __future__ import annotations
 
@@ -56,6 +60,9 @@ def parse():
                    help="launches of the causal forwards on the same workloads (0: skip)")
     p.add_argument("--d256-reps", type=int, default=20,
                    help="launches of the head-dim-256 forwards, B2 H8 N8192 (0: skip)")
+    p.add_argument("--c2-reps", type=int, default=20,
+                   help="launches of the bf16 forward on B2 H32 N4096 d128, non-causal and causal "
+                        "(0: skip)")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run one plain 256 MiB device copy (untimed), the reference that "
                         "scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -138,9 +145,9 @@ def time_reps(fn, reps: int, stream) -> float:
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: attention heads are independent and this build "
-              "has no multi-GPU path (see the sharding notes in the design document).",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (attention "
+              "heads are independent, so several GPUs would each take a share of the heads, "
+              "with no communication).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -353,6 +360,27 @@ def main():
                               "ms": round(t_a16 * 1e3, 4)},
             "finite": bool(torch.isfinite(o2).all().item())}
         del x256, q2, k2, v2, o2, l2
+    if a.c2_reps > 0 and a.d == 128:
+        # The bf16 workload B2 H32 N4096 d128 (N(0,1), seed 1), both masks.
+        print(f"[bench] B2 H32 N4096 forwards: {a.c2_reps} launches each", file=sys.stderr,
+              flush=True)
+        wc2 = workloads.Workload("attn_fwd_b2h32n4096d128", 2, 32, 4096, 128, False, seed=1)
+        xc2 = [dev_bf16(x) for x in workloads.gen_qkv(wc2)]
+        oc2 = torch.empty_like(xc2[0])
+        lc2 = torch.empty((2, 32, 4096), dtype=torch.float32, device=dev)
+        res = {"workload": wc2.name, "timing": "median of per-call HIP event times"}
+        for causal in (False, True):
+            t = time_reps(lambda: ea.attn_fwd_bf16(*xc2, causal=causal,
+                                                   softmax_scale=wc2.softmax_scale, out=oc2,
+                                                   lse=lc2), a.c2_reps, stream)
+            f = wc2.flops() / (2 if causal else 1)
+            res["causal" if causal else "non_causal"] = {
+                "value": round(f / t / 1e12, 2),
+                "pct_of_peak": round(100 * f / t / 1e12 / PEAK_BF16_TFLOPS, 2),
+                "ms": round(t * 1e3, 4)}
+        res["finite"] = bool(torch.isfinite(oc2).all().item())
+        out["b2h32n4096"] = res
+        del xc2, oc2, lc2
     if not a.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w16, a.cpu_seconds)

@@ -355,20 +355,31 @@ _Pragma("unroll")                                                               
 #undef LOAD_TILE
 #undef TILE_BODY
 
+  // Epilogue.  Non-causal: bf16 rows stored whole through LDS (every wave is
+  // done with the K/V tiles after the barrier; each wave takes 32 * 2D bytes
+  // of them).  Causal: stored from the accumulator layout directly (the staged
+  // store measured 3% slower in the persistent causal kernel).
   const float lt = sum_halves(l);
   const float inv = sv_prev / lt;
-  if (qi < N) {
-    __bf16* orow = O + head_off + (int64_t)qi * rs;
+  if constexpr (!CAUSAL) {
+    static_assert(G::NW * 32 * 2 * D <= 2 * G::STAGE, "the output rows are staged in the tile buffers");
+    __syncthreads();
+    store_rows_via_lds<D>(smem + wave * 32 * (2 * D), oacc, inv, O, head_off, rs, q0, N, lane);
+    if (qi < N && LSE != nullptr && hh == 0) LSE[(int64_t)bh * N + qi] = (m + __log2f(lt)) * kLn2;
+  } else {
+    if (qi < N) {
+      __bf16* orow = O + head_off + (int64_t)qi * rs;
 #pragma unroll
-    for (int e = 0; e < D / 32; ++e)
+      for (int e = 0; e < D / 32; ++e)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        i32x2 pk;
-        pk[0] = (int)pack_bf16x2(oacc[e][4 * g + 0] * inv, oacc[e][4 * g + 1] * inv);
-        pk[1] = (int)pack_bf16x2(oacc[e][4 * g + 2] * inv, oacc[e][4 * g + 3] * inv);
-        *(i32x2*)(orow + 32 * e + 8 * g + 4 * hh) = pk;
-      }
-    if (LSE != nullptr && hh == 0) LSE[(int64_t)bh * N + qi] = (m + __log2f(lt)) * kLn2;
+        for (int g = 0; g < 4; ++g) {
+          i32x2 pk;
+          pk[0] = (int)pack_bf16x2(oacc[e][4 * g + 0] * inv, oacc[e][4 * g + 1] * inv);
+          pk[1] = (int)pack_bf16x2(oacc[e][4 * g + 2] * inv, oacc[e][4 * g + 3] * inv);
+          *(i32x2*)(orow + 32 * e + 8 * g + 4 * hh) = pk;
+        }
+      if (LSE != nullptr && hh == 0) LSE[(int64_t)bh * N + qi] = (m + __log2f(lt)) * kLn2;
+    }
   }
 }
 

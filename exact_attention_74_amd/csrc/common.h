@@ -85,4 +85,49 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float x0, float x1, float x2, flo
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Epilogue store of one wave's 32 output rows q0 .. q0 + 31 (BSHD, row pitch
+// rs elements, head offset head_off) through the wave's 32-row LDS block ob
+// (32 * 2D bytes, free for the wave to overwrite).  The O^T accumulator
+// (lane l: row q0 + l % 32, columns 32e + 8g + 4h .. +3, h = l / 32) is
+// scaled by inv, rounded to bf16 and written into ob with 16-byte chunk c of
+// row r at chunk position c ^ (r % CPR); the rows then leave LDS in 16-byte
+// lane reads and global stores, CPR lanes per row, so that every row's 2D
+// bytes are written whole by one store instruction rather than in 8-byte
+// pieces from 2D / 8 instructions.  Rows at or past N are not stored.
+typedef int i32x4_st __attribute__((ext_vector_type(4)));
+template <int D>
+__device__ __forceinline__ void store_rows_via_lds(char* ob, const f32x16 (&oacc)[D / 32],
+                                                   float inv, __bf16* __restrict__ O,
+                                                   int64_t head_off, int64_t rs, int q0, int N,
+                                                   int lane) {
+  constexpr int RB = 2 * D;   // bytes per row (a multiple of 16 * CPR)
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  const int li = lane & 31, hh = lane >> 5;
+  // Row li, chunk c sits at li * RB + ((c ^ (li % CPR)) * 16): the lane's base
+  // address XOR the constant 16 c, so one base register serves every chunk.
+  const uint32_t wbase = (uint32_t)(li * RB + (li % CPR) * 16 + 8 * hh);
+#pragma unroll
+  for (int e = 0; e < D / 32; ++e)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      i32x2 pk;
+      pk[0] = (int)pack_bf16x2(oacc[e][4 * g + 0] * inv, oacc[e][4 * g + 1] * inv);
+      pk[1] = (int)pack_bf16x2(oacc[e][4 * g + 2] * inv, oacc[e][4 * g + 3] * inv);
+      *(i32x2*)(ob + (wbase ^ (uint32_t)((4 * e + g) * 16))) = pk;
+    }
+  // Read-back: lane l takes chunk c = l % CPR of row r = i * RPI + l / CPR.
+  // r % CPR = (i * RPI) % CPR + l / CPR with the two terms in disjoint bits,
+  // so the chunk position is c ^ (l / CPR) ^ ((i * RPI) % CPR).
+  constexpr int RPI = 64 / CPR;  // rows per store instruction
+  const int c = lane % CPR, r0 = lane / CPR;
+  const uint32_t rbase = (uint32_t)(r0 * RB + ((c ^ r0) * 16));
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const uint32_t x = (uint32_t)(((i * RPI) % CPR) * 16);
+    const i32x4_st v = *(const i32x4_st*)(ob + i * RPI * RB + (rbase ^ x));
+    const int r = i * RPI + r0;
+    if (q0 + r < N) *(i32x4_st*)(O + head_off + (int64_t)(q0 + r) * rs + 8 * c) = v;
+  }
+}
+
 }  // namespace exattn
