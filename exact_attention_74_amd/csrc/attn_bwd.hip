@@ -141,22 +141,6 @@ __device__ __forceinline__ void copy_offsets(int wave, int lane, uint32_t row_by
   }
 }
 
-// Stores 32 rows x D of a transposed accumulator (lane = row li, d-values
-// 32 e + 8 (v / 4) + 4 h + v % 4 in element v) as bf16, times `mul`.
-template <int D>
-__device__ __forceinline__ void store_rows(__bf16* row_ptr, const f32x16 (&acc)[D / 32], float mul,
-                                           int hh) {
-#pragma unroll
-  for (int e = 0; e < D / 32; ++e)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      i32x2 pk;
-      pk[0] = (int)pack_bf16x2(acc[e][4 * g + 0] * mul, acc[e][4 * g + 1] * mul);
-      pk[1] = (int)pack_bf16x2(acc[e][4 * g + 2] * mul, acc[e][4 * g + 3] * mul);
-      *(i32x2*)(row_ptr + 32 * e + 8 * g + 4 * hh) = pk;
-    }
-}
-
 // ---------------------------------------------------------------------------
 // D_i = sum_c dO[i, c] O[i, c] and LSE_i * log2(e); D / 8 lanes per row.
 template <int D>
@@ -315,7 +299,11 @@ __global__ __launch_bounds__(64 * kNWb, 2) void bwd_dq_kernel(
     if (kb + 1 < nkb) STEP(1, kb + 1, 1);
   }
 #undef STEP
-  if (qi < N) store_rows<D>(dQ + head_off + (int64_t)qi * rs, dqacc, scale, hh);
+  // dQ rows stored whole through LDS (every wave is done with the tiles after
+  // the barrier; each wave takes 32 * 2D bytes of them).
+  static_assert(kNWb * 32 * 2 * D <= 2 * G::STAGE, "the dQ rows are staged in the tile buffers");
+  __syncthreads();
+  store_rows_via_lds<D>(smem + wave * 32 * (2 * D), dqacc, scale, dQ, head_off, rs, q0, N, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -480,10 +468,13 @@ __global__ __launch_bounds__(64 * kNWb, (D == 64 && CAUSAL) ? 2 : 1) void bwd_dk
     if (qt < nqt) STEP(0, qt);
   }
 #undef STEP
-  if (kj < N) {
-    store_rows<D>(dK + kv_off + (int64_t)kj * rs_kv, dkacc, scale, hh);
-    store_rows<D>(dV + kv_off + (int64_t)kj * rs_kv, dvacc, 1.f, hh);
-  }
+  // dK and dV rows stored whole through LDS (every wave is done with the
+  // tiles after the barrier; each wave takes 2 * 32 * 2D bytes of them).
+  static_assert(kNWb * 2 * 32 * 2 * D <= 2 * G::STAGE, "the dK/dV rows are staged in the tile buffers");
+  __syncthreads();
+  char* ob = tiles + wave * 2 * 32 * (2 * D);
+  store_rows_via_lds<D>(ob, dkacc, scale, dK, kv_off, rs_kv, k0w, N, lane);
+  store_rows_via_lds<D>(ob + 32 * (2 * D), dvacc, 1.f, dV, kv_off, rs_kv, k0w, N, lane);
 }
 
 template <int D, bool CAUSAL>
