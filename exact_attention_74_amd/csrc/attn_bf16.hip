@@ -376,16 +376,25 @@ __global__ __launch_bounds__(64 * NW, D > 128 ? 1 : 2) void attn_fwd_bf16_kernel
     int s = blockIdx.x, second = 0;  // unit (or block) slot; which block of the unit
 #pragma nounroll
     while (s < nslot) {
-      const int u = xcd_remap ? (s & 7) * (nslot >> 3) + (s >> 3) : s;
-      int bh, qblk, last = 1;
-      if (nunits > 0) {
-        const int p = u % npair;
-        bh = u / npair;
-        qblk = second ? p : nqb - 1 - p;
-        last = second || p == nqb - 1 - p;
+      // Work items per query head: units (pairs) or single blocks.  With
+      // xcd_remap, slot s runs on XCD s % 8 (the grid is a multiple of 8),
+      // which takes the K/V head groups x, x + 8, ... as in the non-causal
+      // kernel.
+      const int per = nunits > 0 ? npair : nqb;
+      int bh, item, qblk, last = 1;
+      if (xcd_remap) {
+        const int g = H / Hkv, x = s & 7, j = s >> 3, rem = j % (g * per);
+        bh = ((j / (g * per)) * 8 + x) * g + rem / per;
+        item = rem % per;
       } else {
-        bh = u / nqb;
-        qblk = nqb - 1 - u % nqb;
+        bh = s / per;
+        item = s % per;
+      }
+      if (nunits > 0) {
+        qblk = second ? item : nqb - 1 - item;
+        last = second || item == nqb - 1 - item;
+      } else {
+        qblk = nqb - 1 - item;
       }
       attend_block<D, CAUSAL, NW>(smem, Q, K, V, O, LSE, H, Hkv, N, scale_log2, bh, qblk);
       if (last) {
@@ -425,9 +434,9 @@ hipError_t launch_nw(const void* q, const void* k, const void* v, void* o, float
       grid = units < slots ? units : slots;
     }
   }
-  // non-persistent: the K/V head groups (B * Hkv of them) split evenly over the XCDs
-  const int remap = (nunits > 0 ? (grid % 8 == 0 && nunits % 8 == 0) : ((int64_t)B * Hkv) % 8 == 0)
-                        ? 1 : 0;
+  // the K/V head groups (B * Hkv of them) split evenly over the 8 XCDs, and a
+  // persistent grid a multiple of 8 (each slot stays on one XCD)
+  const int remap = (((int64_t)B * Hkv) % 8 == 0 && grid % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, NW>), dim3((unsigned)grid), dim3(64 * NW), 0,
                      stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse,
                      H, Hkv, N, scale * kLog2e, nqb, remap, (int)nunits);
