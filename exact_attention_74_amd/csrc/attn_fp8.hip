@@ -384,8 +384,9 @@ _Pragma("unroll")                                                               
 }
 
 // Non-causal (and causal at d = 256): one workgroup per (b, h, query block),
-// causal blocks heaviest first; with xcd_remap one head's blocks run on one
-// XCD.  Causal at d <= 128: as the bf16 kernel, persistent slots over units of
+// causal blocks heaviest first; with xcd_remap the query heads of one K/V
+// head run on one XCD, and XCD x takes the K/V head groups x, x + 8, ...
+// Causal at d <= 128: as the bf16 kernel, persistent slots over units of
 // two query blocks (nqb-1-p, p) of equal total cost when nunits > 0, one
 // workgroup per block (heaviest first) when nunits == 0.  (The report's
 // section 5.1 lists the persistent kernel as not yet joined with its FP8
@@ -399,10 +400,19 @@ __global__ __launch_bounds__(64 * waves<D>(), 1) void attn_fwd_fp8_kernel(
   using G = Geo8<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * G::STAGE];
   if constexpr (!persistent8<D, CAUSAL>()) {
-    int L = blockIdx.x;
-    if (xcd_remap) L = (L & 7) * (gridDim.x >> 3) + (L >> 3);
-    const int qb = L % nqb;
-    attend_block8<D, CAUSAL>(smem, Q, K, V, SQ, SK, SV, O, LSE, H, Hkv, N, scale_log2, L / nqb,
+    // With xcd_remap, XCD x (the hardware deals workgroups round robin) takes
+    // the K/V head groups x, x + 8, ..., all query blocks of a group together.
+    const int L = blockIdx.x;
+    int bh, qb;
+    if (xcd_remap) {
+      const int g = H / Hkv, x = L & 7, j = L >> 3, rem = j % (g * nqb);
+      bh = ((j / (g * nqb)) * 8 + x) * g + rem / nqb;
+      qb = rem % nqb;
+    } else {
+      bh = L / nqb;
+      qb = L % nqb;
+    }
+    attend_block8<D, CAUSAL>(smem, Q, K, V, SQ, SK, SV, O, LSE, H, Hkv, N, scale_log2, bh,
                              CAUSAL ? nqb - 1 - qb : qb);
   } else {
     const int npair = (nqb + 1) / 2;
@@ -410,16 +420,24 @@ __global__ __launch_bounds__(64 * waves<D>(), 1) void attn_fwd_fp8_kernel(
     int s = blockIdx.x, second = 0;
 #pragma nounroll
     while (s < nslot) {
-      const int u = xcd_remap ? (s & 7) * (nslot >> 3) + (s >> 3) : s;
-      int bh, qblk, last = 1;
-      if (nunits > 0) {
-        const int p = u % npair;
-        bh = u / npair;
-        qblk = second ? p : nqb - 1 - p;
-        last = second || p == nqb - 1 - p;
+      // Work items per query head: units (pairs) or single blocks; with
+      // xcd_remap, slot s stays on XCD s % 8, which takes the K/V head groups
+      // x, x + 8, ... as above.
+      const int per = nunits > 0 ? npair : nqb;
+      int bh, item, qblk, last = 1;
+      if (xcd_remap) {
+        const int g = H / Hkv, x = s & 7, j = s >> 3, rem = j % (g * per);
+        bh = ((j / (g * per)) * 8 + x) * g + rem / per;
+        item = rem % per;
       } else {
-        bh = u / nqb;
-        qblk = nqb - 1 - u % nqb;
+        bh = s / per;
+        item = s % per;
+      }
+      if (nunits > 0) {
+        qblk = second ? item : nqb - 1 - item;
+        last = second || item == nqb - 1 - item;
+      } else {
+        qblk = nqb - 1 - item;
       }
       attend_block8<D, CAUSAL>(smem, Q, K, V, SQ, SK, SV, O, LSE, H, Hkv, N, scale_log2, bh, qblk);
       if (last) {
@@ -456,7 +474,9 @@ hipError_t launch(const void* q8, const void* k8, const void* v8, const float* s
       grid = units < slots ? units : slots;
     }
   }
-  const int remap = (grid % 8 == 0 && (nunits == 0 || nunits % 8 == 0)) ? 1 : 0;
+  // the K/V head groups (B * Hkv of them) split evenly over the 8 XCDs, and a
+  // persistent grid a multiple of 8 (each slot stays on one XCD)
+  const int remap = (((int64_t)B * Hkv) % 8 == 0 && grid % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(64 * waves<D>()), 0,
                      stream, (const uint8_t*)q8, (const uint8_t*)k8, (const uint8_t*)v8, sq, sk, sv,
                      (__bf16*)o, lse, H, Hkv, N, scale * kLog2e, nqb, remap, (int)nunits);
