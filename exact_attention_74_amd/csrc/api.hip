@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "exattn.h"
 #include "launch.h"
 
@@ -13,11 +15,33 @@ constexpr int64_t kMaxN = int64_t(1) << 24;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// Byte ranges [a, a+na) and [b, b+nb) overlap.
-bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
-  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
-  return pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
+// A byte range [p, p + n) of device memory; p == NULL (an optional argument
+// left out) or n == 0 takes part in no overlap.
+struct Span {
+  const void* p;
+  int64_t n;
+};
+
+bool overlap(Span a, Span b) {
+  if (!a.p || !b.p || a.n <= 0 || b.n <= 0) return false;
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a.p), pb = reinterpret_cast<uintptr_t>(b.p);
+  return pa < pb + (uintptr_t)b.n && pb < pa + (uintptr_t)a.n;
 }
+
+// True when an output overlaps an input or another output (inputs may share
+// memory with each other: they are only read).
+bool aliased(std::initializer_list<Span> outs, std::initializer_list<Span> ins) {
+  for (auto o = outs.begin(); o != outs.end(); ++o) {
+    for (const Span& i : ins)
+      if (overlap(*o, i)) return true;
+    for (auto o2 = o + 1; o2 != outs.end(); ++o2)
+      if (overlap(*o, *o2)) return true;
+  }
+  return false;
+}
+
+// fp32 scale slots per (b, h) of a sequence of N rows (one per 128 rows).
+int64_t scale_blocks(int N) { return ((int64_t)N + 127) / 128; }
 
 // elt: bytes per element of the Q/K/V inputs.  One batch entry of a tensor
 // (N x H x d elements) must stay below 2 GiB: kernels address a head's rows
@@ -53,7 +77,9 @@ const char* exattn_strerror(int code) {
       return "unsupported shape (negative size, d not in {64,128,256} (backward: {64,128}), too "
              "large, or H not a multiple of H_kv)";
     case EXATTN_ERR_ALIGN: return "pointer not aligned (tensors 16 bytes, scales/LSE 4 bytes)";
-    case EXATTN_ERR_VALUE: return "invalid value (softmax_scale, causal, block_rows, or aliasing output)";
+    case EXATTN_ERR_VALUE:
+      return "invalid value (softmax_scale, causal, block_rows, or an output overlapping an "
+             "input or another output)";
     case EXATTN_ERR_HIP: return "HIP error (no device or kernel launch failed)";
     default: return "unknown error code";
   }
@@ -73,10 +99,8 @@ int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, void* o, floa
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       (lse && !aligned(lse, 4)))
     return EXATTN_ERR_ALIGN;
-  if (overlap(o, bytes, q, bytes) || overlap(o, bytes, k, kv_bytes) ||
-      overlap(o, bytes, v, kv_bytes))
+  if (aliased({{o, bytes}, {lse, (int64_t)B * H * N * 4}}, {{q, bytes}, {k, kv_bytes}, {v, kv_bytes}}))
     return EXATTN_ERR_VALUE;
-  if (lse && overlap(lse, (int64_t)B * H * N * 4, o, bytes)) return EXATTN_ERR_VALUE;
   return hip_status(exattn::launch_attn_fwd_bf16(q, k, v, o, lse, B, H, H_kv, N, d, causal != 0,
                                                  softmax_scale, (hipStream_t)stream));
 }
@@ -102,10 +126,12 @@ int attn_fwd_fp8_gqa(const void* q8, const void* k8, const void* v8, const float
       (lse && !aligned(lse, 4)))
     return EXATTN_ERR_ALIGN;
   const int64_t out_bytes = 2 * in_bytes;
-  if (overlap(o, out_bytes, q8, in_bytes) || overlap(o, out_bytes, k8, kv_bytes) ||
-      overlap(o, out_bytes, v8, kv_bytes))
+  const int64_t sq_bytes = (int64_t)B * H * scale_blocks(N) * 4;
+  const int64_t skv_bytes = (int64_t)B * H_kv * scale_blocks(N) * 4;
+  if (aliased({{o, out_bytes}, {lse, (int64_t)B * H * N * 4}},
+              {{q8, in_bytes}, {k8, kv_bytes}, {v8, kv_bytes}, {q_scale, sq_bytes},
+               {k_scale, skv_bytes}, {v_scale, skv_bytes}}))
     return EXATTN_ERR_VALUE;
-  if (lse && overlap(lse, (int64_t)B * H * N * 4, o, out_bytes)) return EXATTN_ERR_VALUE;
   return hip_status(exattn::launch_attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B,
                                                 H, H_kv, N, d, causal != 0, softmax_scale,
                                                 (hipStream_t)stream));
@@ -145,16 +171,10 @@ int attn_bwd_bf16_gqa(const void* q, const void* k, const void* v, const void* o
   const int64_t ws_bytes = 2 * lse_bytes;
   const int64_t kv_bytes = (int64_t)B * N * H_kv * d * 2;
   // Outputs and workspace must not overlap any input or each other.
-  const void* in[] = {q, k, v, o, dout, lse};
-  const int64_t in_n[] = {bytes, kv_bytes, kv_bytes, bytes, bytes, lse_bytes};
-  const void* out[] = {dq, dk, dv, workspace};
-  const int64_t out_n[] = {bytes, kv_bytes, kv_bytes, ws_bytes};
-  for (int i = 0; i < 4; ++i) {
-    for (int j = 0; j < 6; ++j)
-      if (overlap(out[i], out_n[i], in[j], in_n[j])) return EXATTN_ERR_VALUE;
-    for (int j = i + 1; j < 4; ++j)
-      if (overlap(out[i], out_n[i], out[j], out_n[j])) return EXATTN_ERR_VALUE;
-  }
+  if (aliased({{dq, bytes}, {dk, kv_bytes}, {dv, kv_bytes}, {workspace, ws_bytes}},
+              {{q, bytes}, {k, kv_bytes}, {v, kv_bytes}, {o, bytes}, {dout, bytes},
+               {lse, lse_bytes}}))
+    return EXATTN_ERR_VALUE;
   return hip_status(exattn::launch_attn_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, workspace, B,
                                                  H, H_kv, N, d, causal != 0, softmax_scale,
                                                  (hipStream_t)stream));
@@ -177,7 +197,9 @@ int blockquant_hadamard(const void* x, void* x8, float* scale, const float* sign
   if (!x || !x8 || !scale) return EXATTN_ERR_NULL;
   if (!aligned(x, 16) || !aligned(x8, 16) || !aligned(scale, 4) || (signs && !aligned(signs, 4)))
     return EXATTN_ERR_ALIGN;
-  if (overlap(x8, n, x, 2 * n)) return EXATTN_ERR_VALUE;
+  const int64_t s_bytes = (int64_t)B * H * scale_blocks(N) * 4;
+  if (aliased({{x8, n}, {scale, s_bytes}}, {{x, 2 * n}, {signs, (int64_t)d * 4}}))
+    return EXATTN_ERR_VALUE;
   return hip_status(
       exattn::launch_blockquant(x, x8, scale, signs, B, H, N, d, block_rows, (hipStream_t)stream));
 }
@@ -195,7 +217,12 @@ int rope_blockquant_hadamard(const void* x, void* x8, float* scale, const float*
   if (!aligned(x, 16) || !aligned(x8, 16) || !aligned(scale, 4) || (signs && !aligned(signs, 4)) ||
       !aligned(rope_cos, 16) || !aligned(rope_sin, 16))
     return EXATTN_ERR_ALIGN;
-  if (overlap(x8, n, x, 2 * n)) return EXATTN_ERR_VALUE;
+  const int64_t s_bytes = (int64_t)B * H * scale_blocks(N) * 4;
+  const int64_t table_bytes = (int64_t)N * (d / 2) * 4;
+  if (aliased({{x8, n}, {scale, s_bytes}},
+              {{x, 2 * n}, {signs, (int64_t)d * 4}, {rope_cos, table_bytes},
+               {rope_sin, table_bytes}}))
+    return EXATTN_ERR_VALUE;
   return hip_status(exattn::launch_rope_blockquant(x, x8, scale, signs, rope_cos, rope_sin,
                                                    rope_interleaved != 0, B, H, N, d, block_rows,
                                                    (hipStream_t)stream));

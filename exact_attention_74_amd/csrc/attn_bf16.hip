@@ -213,13 +213,12 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
     qf[t] = (qi < N) ? *(const bf16x8*)(Q + head_off + (int64_t)qi * rs + 16 * t + 8 * hh) : z;
   }
 
-  // Buffer descriptors over this head's K and V rows; row n >= N is out of
-  // range (reads return 0).
+  // This head's K and V rows end at byte nbytes; each tile's copies go
+  // through a descriptor that starts at the tile's first row and ends there,
+  // so rows n >= N read as zeros.
   const uint32_t nbytes = (uint32_t)(((int64_t)(N - 1) * rs_kv + D) * 2);
-  const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(K + kv_off), (short)0, nbytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(V + kv_off), (short)0, nbytes, 0x00020000);
+  const __bf16* kh = K + kv_off;
+  const __bf16* vh = V + kv_off;
   const uint32_t row_bytes = (uint32_t)(rs_kv * 2);
 
   // Per-lane global byte offsets of the chunks this lane deposits into LDS.
@@ -233,11 +232,13 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
   }
 #define LOAD_TILE(stage, k0)                                                                    \
   do {                                                                                          \
-    const uint32_t soff_ = (uint32_t)(k0) * row_bytes;                                          \
+    const uint32_t off_ = (uint32_t)(k0) * row_bytes;                                           \
+    const __amdgpu_buffer_rsrc_t rk_ = tile_rsrc(kh, off_, nbytes);                             \
+    const __amdgpu_buffer_rsrc_t rv_ = tile_rsrc(vh, off_, nbytes);                             \
     _Pragma("unroll") for (int i_ = 0; i_ < LOADS; ++i_) {                                   \
       char* dst_ = smem + (wave * LOADS + i_) * 1024;                                          \
-      copy_to_lds16(rk, dst_ + G::koff(stage), voff_k[i_], soff_);                              \
-      copy_to_lds16(rv, dst_ + G::VBASE + G::voff(stage), voff_v[i_], soff_);                   \
+      copy_to_lds16(rk_, dst_ + G::koff(stage), voff_k[i_]);                                    \
+      copy_to_lds16(rv_, dst_ + G::VBASE + G::voff(stage), voff_v[i_]);                         \
     }                                                                                           \
   } while (0)
 

@@ -27,8 +27,8 @@
 // are computed twice (seven matrix products instead of five) and every
 // result is deterministic.
 //
-// LDS tiles are 64 rows, copied by buffer_load ... lds (reads past the end of
-// the sequence return zeros) and double-buffered, as in the forward.  A tile
+// LDS tiles are 64 rows, copied by buffer_load ... lds (rows past the end of
+// the sequence read as zeros) and double-buffered, as in the forward.  A tile
 // that is read both row-wise (ds_read_b128, an A operand) and transposed
 // (ds_read_b64_tr_b16) uses the chunk swizzle swz_b, free of bank conflicts
 // for both patterns.
@@ -213,22 +213,23 @@ __global__ __launch_bounds__(64 * kNWb, 2) void bwd_dq_kernel(
   // K/V head of this query head (grouped-query attention: H / Hkv per group)
   const int64_t rs_kv = (int64_t)Hkv * D;
   const int64_t kv_off = ((int64_t)b * N * Hkv + h / (H / Hkv)) * D;
+  // Descriptors over the head's K/V rows (ending at byte nbytes); the tile's
+  // position goes into the range-checked per-lane offset, so rows n >= N read
+  // as zeros.
   const uint32_t nbytes = (uint32_t)(((int64_t)(N - 1) * rs_kv + D) * 2);
-  const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(K + kv_off), (short)0, nbytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(V + kv_off), (short)0, nbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rk = tile_rsrc(K + kv_off, 0, nbytes);
+  const __amdgpu_buffer_rsrc_t rv = tile_rsrc(V + kv_off, 0, nbytes);
   const uint32_t row_bytes = (uint32_t)(rs_kv * 2);
   uint32_t voff_k[LOADS], voff_v[LOADS];
   copy_offsets<D, LOADS, 1>(wave, lane, row_bytes, voff_k);
   copy_offsets<D, LOADS, 0>(wave, lane, row_bytes, voff_v);
   auto load_tile = [&](int stage, int k0) __attribute__((always_inline)) {
-    const uint32_t soff = (uint32_t)k0 * row_bytes;
+    const uint32_t off = (uint32_t)k0 * row_bytes;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       char* dst = smem + stage * G::STAGE + (wave * LOADS + i) * 1024;
-      copy_to_lds16(rk, dst, voff_k[i], soff);
-      copy_to_lds16(rv, dst + G::TILE, voff_v[i], soff);
+      copy_to_lds16(rk, dst, voff_k[i] + off);
+      copy_to_lds16(rv, dst + G::TILE, voff_v[i] + off);
     }
   };
 
@@ -348,39 +349,37 @@ __global__ __launch_bounds__(64 * kNWb, (D == 64 && CAUSAL) ? 2 : 1) void bwd_dk
     vt[t] = kj < N ? *(const bf16x8*)(V + kv_off + (int64_t)kj * rs_kv + 16 * t + 8 * hh) : z;
   }
 
+  // Descriptors over a head's Q and dO rows (ending at byte nbytes) and its
+  // LSE and D vectors (4 N bytes); the tile's position goes into the
+  // range-checked per-lane offset, so rows n >= N read as zeros.
   const uint32_t nbytes = (uint32_t)(((int64_t)(N - 1) * rs + D) * 2);
   // Q, dO, LSE and D of query head h (set per head of the group)
   __amdgpu_buffer_rsrc_t rq, rg, rl, rd;
   auto set_head = [&](int h) __attribute__((always_inline)) {
     const int64_t head_off = ((int64_t)b * N * H + h) * D;
     const int64_t bh = (int64_t)b * H + h;
-    rq = __builtin_amdgcn_make_buffer_rsrc((void*)(Q + head_off), (short)0, nbytes, 0x00020000);
-    rg = __builtin_amdgcn_make_buffer_rsrc((void*)(dO + head_off), (short)0, nbytes, 0x00020000);
-    rl = __builtin_amdgcn_make_buffer_rsrc((void*)(L2 + bh * N), (short)0, (uint32_t)N * 4,
-                                           0x00020000);
-    rd = __builtin_amdgcn_make_buffer_rsrc((void*)(Drow + bh * N), (short)0, (uint32_t)N * 4,
-                                           0x00020000);
+    rq = tile_rsrc(Q + head_off, 0, nbytes);
+    rg = tile_rsrc(dO + head_off, 0, nbytes);
+    rl = tile_rsrc(L2 + bh * N, 0, (uint32_t)N * 4);
+    rd = tile_rsrc(Drow + bh * N, 0, (uint32_t)N * 4);
   };
   const uint32_t row_bytes = (uint32_t)(rs * 2);
   uint32_t voff[LOADS];
   copy_offsets<D, LOADS, 1>(wave, lane, row_bytes, voff);
   auto load_tile = [&](int stage, int i0) __attribute__((always_inline)) {
-    const uint32_t soff = (uint32_t)i0 * row_bytes;
+    const uint32_t off = (uint32_t)i0 * row_bytes;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       char* dst = tiles + stage * G::STAGE + (wave * LOADS + i) * 1024;
-      copy_to_lds16(rq, dst, voff[i], soff);
-      copy_to_lds16(rg, dst + G::TILE, voff[i], soff);
+      copy_to_lds16(rq, dst, voff[i] + off);
+      copy_to_lds16(rg, dst + G::TILE, voff[i] + off);
     }
-    // 64 floats of LSE*log2e (lanes 0-15) and of D (lanes 16-31), by wave 0;
-    // lane i's 16 bytes land at 16 i, so D follows LSE.
-    if (wave == 0 && lane < 32) {
-      char* dst = smem + stage * 512;
-      if (lane < 16)
-        copy_to_lds16(rl, dst, (uint32_t)lane * 16, (uint32_t)i0 * 4);
-      else
-        copy_to_lds16(rd, dst, (uint32_t)(lane - 16) * 16, (uint32_t)i0 * 4);
-    }
+    // 64 floats of LSE*log2e (wave 0) and of D (wave 1), lanes 0-15; lane i's
+    // 16 bytes land at 16 i, and D follows LSE.  The descriptor is chosen by
+    // the wave index (a scalar), so it stays in scalar registers.
+    if (wave < 2 && lane < 16)
+      copy_to_lds16(wave == 0 ? rl : rd, smem + stage * 512 + wave * 256,
+                    (uint32_t)i0 * 4 + (uint32_t)lane * 16);
   };
 
   const uint32_t base = lds_addr(tiles);

@@ -65,9 +65,12 @@ struct Geo8 {
   }
 };
 
+// 16-byte-per-lane copy global -> LDS (lane i's chunk lands at lds_dst + 16 i);
+// the scalar offset is 0 because only the per-lane offset is range-checked:
+// the tile's position is in the descriptor (tile_rsrc).
 __device__ __forceinline__ void copy_to_lds16(__amdgpu_buffer_rsrc_t r, char* lds_dst,
-                                              uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 16, voff, soff, 0, 0);
+                                              uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 16, voff, 0, 0, 0);
 }
 
 // LDS byte address of a generic pointer into LDS.
@@ -181,11 +184,11 @@ __device__ __forceinline__ void attend_block8(
     qf[t] = (qi < N) ? *(const i32x8*)(Q + head_off + (int64_t)qi * rs + 64 * t + 32 * hh) : z;
   }
 
+  // This head's K/V rows end at byte nbytes; per-tile descriptors start at the
+  // tile's first row and end there, so rows n >= N read as zeros.
   const uint32_t nbytes = (uint32_t)((int64_t)(N - 1) * rs_kv + D);
-  const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(K + kv_off), (short)0, nbytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(V + kv_off), (short)0, nbytes, 0x00020000);
+  const uint8_t* kh = K + kv_off;
+  const uint8_t* vh = V + kv_off;
   const uint32_t row_bytes = (uint32_t)rs_kv;
   uint32_t voff_k[G::LOADS], voff_v[G::LOADS];
 #pragma unroll
@@ -197,11 +200,13 @@ __device__ __forceinline__ void attend_block8(
   }
 #define LOAD_TILE(stage, k0)                                                                    \
   do {                                                                                          \
-    const uint32_t soff_ = (uint32_t)(k0) * row_bytes;                                          \
+    const uint32_t off_ = (uint32_t)(k0) * row_bytes;                                           \
+    const __amdgpu_buffer_rsrc_t rk_ = tile_rsrc(kh, off_, nbytes);                             \
+    const __amdgpu_buffer_rsrc_t rv_ = tile_rsrc(vh, off_, nbytes);                             \
     _Pragma("unroll") for (int i_ = 0; i_ < G::LOADS; ++i_) {                                   \
       char* dst_ = smem + (wave * G::LOADS + i_) * 1024;                                        \
-      copy_to_lds16(rk, dst_ + G::koff(stage), voff_k[i_], soff_);                              \
-      copy_to_lds16(rv, dst_ + G::VBASE + G::voff(stage), voff_v[i_], soff_);                   \
+      copy_to_lds16(rk_, dst_ + G::koff(stage), voff_k[i_]);                                    \
+      copy_to_lds16(rv_, dst_ + G::VBASE + G::voff(stage), voff_v[i_]);                         \
     }                                                                                           \
   } while (0)
 

@@ -85,6 +85,18 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float x0, float x1, float x2, flo
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Raw buffer descriptor over bytes [off, total) of the region at base (off <
+// total).  Loads through it at per-lane offset x read base + off + x when
+// off + x < total and return zeros otherwise.  The hardware range check
+// applies to the per-lane (VGPR) offset and not to the scalar offset, so a
+// tile's start must be carried here, in the descriptor's base and size,
+// for rows past the end of the region to read as zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, uint32_t off,
+                                                            uint32_t total) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)base + off), (short)0,
+                                           total - off, 0x00020000);
+}
+
 // Epilogue store of one wave's 32 output rows q0 .. q0 + 31 (BSHD, row pitch
 // rs elements, head offset head_off) through the wave's 32-row LDS block ob
 // (32 * 2D bytes, free for the wave to overwrite).  The O^T accumulator

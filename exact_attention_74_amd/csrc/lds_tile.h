@@ -43,10 +43,12 @@ struct Geo {
 };
 
 // Asynchronous 16-byte-per-lane copy global -> LDS; lane i's chunk lands at
-// lds_dst + 16 i (lds_dst is wave-uniform).
+// lds_dst + 16 i (lds_dst is wave-uniform).  The scalar offset is always 0:
+// the range check of a raw buffer covers the per-lane offset only, so a tile's
+// position goes into the descriptor (tile_rsrc), never into soffset.
 __device__ __forceinline__ void copy_to_lds16(__amdgpu_buffer_rsrc_t r, char* lds_dst,
-                                              uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 16, voff, soff, 0, 0);
+                                              uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 16, voff, 0, 0, 0);
 }
 
 // LDS byte address of a generic pointer into LDS.
