@@ -48,6 +48,10 @@ RESTYPES = {"exattn_strerror": ctypes.c_char_p, "attn_bwd_bf16_workspace_bytes":
 
 ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_VALUE, ERR_HIP = -1, -2, -3, -4, -5
 
+# torch device type that every tensor argument must have (HIP devices appear
+# as "cuda" in PyTorch-ROCm)
+_DEVICE_TYPE = "cuda"
+
 _lib = None
 
 
@@ -84,13 +88,26 @@ def _stream_ptr(t: torch.Tensor) -> int:
 def _check_bshd(name: str, t: torch.Tensor, dtype) -> tuple[int, int, int, int]:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if t.device.type != _DEVICE_TYPE:
         raise ValueError(f"{name} must be on a HIP device (got {t.device})")
     if t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
         raise TypeError(f"{name} must have dtype {dtype} (got {t.dtype})")
     if t.dim() != 4 or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous 4-D BSHD tensor")
     return tuple(t.shape)
+
+
+def _check_out(name: str, t, shape, dtype, device) -> None:
+    """A caller-supplied output (or a scale input) must match exactly: the C
+    ABI sees only a pointer, so a short buffer would be overrun on the GPU."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    dtypes = dtype if isinstance(dtype, tuple) else (dtype,)
+    if (t.dtype not in dtypes or tuple(t.shape) != tuple(shape) or not t.is_contiguous()
+            or t.device != device):
+        raise ValueError(f"{name} must be a contiguous {dtypes[0]} tensor of shape "
+                         f"{tuple(shape)} on {device} (got {t.dtype} {tuple(t.shape)} on "
+                         f"{t.device}{'' if t.is_contiguous() else ', not contiguous'})")
 
 
 def _call(fn: str, *args) -> None:
@@ -120,10 +137,17 @@ def _bf16(fn, q, k, v, causal, softmax_scale, out, lse):
                     _check_bshd("v", v, torch.bfloat16), fn.endswith("_gqa"))
     B, N, H, d = shape
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    for name, t in (("k", k), ("v", v)):
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on q's device")
     if out is None:
         out = torch.empty_like(q)
+    else:
+        _check_out("out", out, (B, N, H, d), torch.bfloat16, q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        _check_out("lse", lse, (B, H, N), torch.float32, q.device)
     heads = (H, Hkv) if fn.endswith("_gqa") else (H,)
     _call(fn, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
           B, *heads, N, d, int(bool(causal)), scale, _stream_ptr(q))
@@ -143,6 +167,21 @@ def attn_fwd_bf16_gqa(q, k, v, causal: bool = False, softmax_scale: float | None
     return _bf16("attn_fwd_bf16_gqa", q, k, v, causal, softmax_scale, out, lse)
 
 
+def _quant_outputs(x, out, scale):
+    """The pre-pass outputs: allocated here, or checked when the caller passes them."""
+    B, N, H, d = x.shape
+    nsb = (N + 127) // 128
+    if out is None:
+        out = torch.empty((B, N, H, d), dtype=torch.uint8, device=x.device)
+    else:
+        _check_out("out", out, (B, N, H, d), (torch.uint8, torch.float8_e4m3fn), x.device)
+    if scale is None:
+        scale = torch.empty((B, H, nsb), dtype=torch.float32, device=x.device)
+    else:
+        _check_out("scale", scale, (B, H, nsb), torch.float32, x.device)
+    return out, scale
+
+
 def blockquant_hadamard(x, signs: torch.Tensor | None = None, block_rows: int = 128,
                         out: torch.Tensor | None = None, scale: torch.Tensor | None = None):
     """Rotate (if ``signs``) and block-quantise a bf16 BSHD tensor to e4m3.
@@ -154,10 +193,7 @@ def blockquant_hadamard(x, signs: torch.Tensor | None = None, block_rows: int = 
         if signs.device != x.device or signs.dtype != torch.float32 or signs.numel() != d:
             raise ValueError("signs must be d float32 values on the same device")
         signs = signs.contiguous()
-    if out is None:
-        out = torch.empty((B, N, H, d), dtype=torch.uint8, device=x.device)
-    if scale is None:
-        scale = torch.empty((B, H, (N + 127) // 128), dtype=torch.float32, device=x.device)
+    out, scale = _quant_outputs(x, out, scale)
     _call("blockquant_hadamard", x.data_ptr(), out.data_ptr(), scale.data_ptr(),
           signs.data_ptr() if signs is not None else None, B, H, N, d, int(block_rows),
           _stream_ptr(x))
@@ -171,14 +207,20 @@ def _fp8(fn, q8, k8, v8, q_scale, k_scale, v_scale, causal, softmax_scale, out, 
                     _check_bshd("v8", v8, codes), fn.endswith("_gqa"))
     B, N, H, d = shape
     nsb = (N + 127) // 128
+    for name, t in (("k8", k8), ("v8", v8)):
+        if t.device != q8.device:
+            raise ValueError(f"{name} must be on q8's device")
     for name, s, h in (("q_scale", q_scale, H), ("k_scale", k_scale, Hkv), ("v_scale", v_scale, Hkv)):
-        if s.dtype != torch.float32 or tuple(s.shape) != (B, h, nsb) or not s.is_contiguous():
-            raise ValueError(f"{name} must be contiguous float32 [B, {h}, ceil(N/128)]")
+        _check_out(name, s, (B, h, nsb), torch.float32, q8.device)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     if out is None:
         out = torch.empty((B, N, H, d), dtype=torch.bfloat16, device=q8.device)
+    else:
+        _check_out("out", out, (B, N, H, d), torch.bfloat16, q8.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    else:
+        _check_out("lse", lse, (B, H, N), torch.float32, q8.device)
     heads = (H, Hkv) if fn.endswith("_gqa") else (H,)
     _call(fn, q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), q_scale.data_ptr(),
           k_scale.data_ptr(), v_scale.data_ptr(), out.data_ptr(), lse.data_ptr(), B, *heads, N, d,
@@ -200,10 +242,7 @@ def rope_blockquant_hadamard(x, cos, sin, interleaved: bool, signs: torch.Tensor
         if signs.device != x.device or signs.dtype != torch.float32 or signs.numel() != d:
             raise ValueError("signs must be d float32 values on the same device")
         signs = signs.contiguous()
-    if out is None:
-        out = torch.empty((B, N, H, d), dtype=torch.uint8, device=x.device)
-    if scale is None:
-        scale = torch.empty((B, H, (N + 127) // 128), dtype=torch.float32, device=x.device)
+    out, scale = _quant_outputs(x, out, scale)
     _call("rope_blockquant_hadamard", x.data_ptr(), out.data_ptr(), scale.data_ptr(),
           signs.data_ptr() if signs is not None else None, cos.data_ptr(), sin.data_ptr(),
           int(bool(interleaved)), B, H, N, d, int(block_rows), _stream_ptr(x))
@@ -243,13 +282,17 @@ def attn_bwd_bf16(q, k, v, o, lse, do, causal: bool = False, softmax_scale: floa
     Hkv = _kv_heads("attn_bwd_bf16", shape, _check_bshd("k", k, torch.bfloat16),
                     _check_bshd("v", v, torch.bfloat16), grouped=True)
     B, N, H, d = shape
-    if (not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32
-            or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous() or lse.device != q.device):
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    for name, t in (("k", k), ("v", v), ("o", o), ("do", do)):
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on q's device")
+    _check_out("lse", lse, (B, H, N), torch.float32, q.device)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    _check_out("dq", dq, (B, N, H, d), torch.bfloat16, q.device)
+    _check_out("dk", dk, tuple(k.shape), torch.bfloat16, q.device)
+    _check_out("dv", dv, tuple(v.shape), torch.bfloat16, q.device)
     nbytes = lib().attn_bwd_bf16_workspace_bytes(B, H, N)
     if nbytes < 0:
         raise ExattnError("attn_bwd_bf16_workspace_bytes", nbytes)

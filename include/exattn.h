@@ -40,6 +40,10 @@
  *               sizes, values, empty problem, NULL, alignment, aliasing; on a validation
  *               error nothing is launched and no output is touched.  No C++
  *               exception crosses the ABI.  Thread-safe.
+ *   Aliasing    no output (O, LSE, e4m3 codes, scales, gradients, workspace)
+ *               may overlap an input (tensors, scales, signs, RoPE tables) or
+ *               another output: EXATTN_ERR_VALUE.  Inputs may overlap each
+ *               other.  Sizes are those of the arguments' documented shapes.
  *   Causal      key j is visible to query i iff j <= i.
  *   Outputs     O is bfloat16 (round to nearest even from fp32);
  *               LSE[b, h, i] = ln sum_j exp(scale * q_i . k_j) over visible
@@ -57,7 +61,7 @@ extern "C" {
 #define EXATTN_ERR_NULL (-1)  /* a required pointer is NULL                        */
 #define EXATTN_ERR_SHAPE (-2) /* negative size, unsupported d, or too large       */
 #define EXATTN_ERR_ALIGN (-3) /* a pointer is not aligned as required             */
-#define EXATTN_ERR_VALUE (-4) /* softmax_scale not finite and > 0, bad block_rows */
+#define EXATTN_ERR_VALUE (-4) /* bad softmax_scale/causal/block_rows, or aliasing */
 #define EXATTN_ERR_HIP (-5)   /* no HIP device, or a launch failed                */
 
 /*

@@ -199,3 +199,31 @@ def test_bwd_gqa_head_counts():
     assert f(*args, 1, 4, 3, 256, 64, 0, 0.125, None) == ea.ERR_SHAPE
     assert f(*args, 1, 4, 0, 256, 64, 0, 0.125, None) == ea.ERR_SHAPE
     assert f(*args, 0, 4, 2, 256, 64, 0, 0.125, None) == 0
+
+
+def test_aliasing_every_output_input_pair():
+    """Every output is checked against every input and every other output,
+    including the scale arrays (B*H*ceil(N/128) floats), signs and RoPE tables."""
+    # bf16 forward: lse against q, k, v, and o against lse
+    assert _bf16(lse=P) == ea.ERR_VALUE
+    assert _bf16(lse=P + P2 + 4) == ea.ERR_VALUE
+    assert _bf16(lse=P + 2 * P2 + 1024) == ea.ERR_VALUE
+    assert _bf16(lse=P + 3 * P2 + 64) == ea.ERR_VALUE
+    # fp8 forward: o and lse against the three scale arrays (2 heads x 2 blocks x 4 B)
+    assert _fp8(o=P + 3 * P2 - 16) == ea.ERR_VALUE        # o ends inside q_scale's start
+    assert _fp8(lse=P + 4 * P2 + 4) == ea.ERR_VALUE       # lse inside k_scale
+    assert _fp8(sv=P + 7 * P2 + 4) == ea.ERR_VALUE        # v_scale inside lse
+    assert _fp8(sq=P + 6 * P2 + 512) == ea.ERR_VALUE      # q_scale inside o
+    # blockquant: scale against x, x8 and signs; x8 against signs
+    assert _bq(s=P + 64) == ea.ERR_VALUE                  # scale inside x
+    assert _bq(s=P + P2 + 64) == ea.ERR_VALUE             # scale inside x8
+    assert _bq(signs=P + 2 * P2 + 4) == ea.ERR_VALUE      # signs inside scale
+    assert _bq(signs=P + P2 + 128) == ea.ERR_VALUE        # signs inside x8
+    assert _bq(signs=P + 2 * P2 + 12) == ea.ERR_VALUE     # signs start in scale's last slot
+    # rope pre-pass: outputs against cos/sin/signs
+    assert _rq(s=P + 3 * P2 + 16) == ea.ERR_VALUE         # scale inside cos
+    assert _rq(x8=P + 4 * P2) == ea.ERR_VALUE             # codes over sin
+    assert _rq(signs=P + P2 + 32) == ea.ERR_VALUE         # signs inside the codes
+    # backward: lse input against the workspace and gradients
+    assert _bwd(dv=P + 5 * P2 + 16) == ea.ERR_VALUE       # dV over the LSE
+
