@@ -67,16 +67,26 @@ def attention_backward(q, k, v, do, scale: float, causal: bool):
 
 
 def attention_backward_heads(q, k, v, do, scale: float, causal: bool, heads):
-    """The same for selected (b, h) pairs only: ``heads`` is an int array
-    [R, 2].  Returns fp64 arrays [R, N, d] for dQ, dK, dV (large workloads are
+    """The same for selected query heads only: ``heads`` is an int array
+    [R, 2] of (b, h) pairs.  Returns fp64 arrays [R, N, d]: dQ of query head
+    (b, h), and dK, dV of the K/V head (b, g) it reads, g = h // (H // H_kv),
+    which are the sums over all query heads of that group (large workloads are
     checked on a few whole heads: every key's gradient needs every query)."""
     q, k, v, do = (np.asarray(x) for x in (q, k, v, do))
     heads = np.asarray(heads, np.int64)
     R, N, d = heads.shape[0], q.shape[1], q.shape[3]
+    H, Hkv = q.shape[2], k.shape[2]
+    r = H // Hkv
     out = [np.empty((R, N, d)) for _ in range(3)]
-    for r, (b, h) in enumerate(heads):
-        sl = lambda x: np.asarray(x[b:b + 1, :, h:h + 1, :], np.float64)  # noqa: E731
-        g = attention_backward(sl(q), sl(k), sl(v), sl(do), scale, causal)
-        for t in range(3):
-            out[t][r] = g[t][0, :, 0, :]
+    for i, (b, h) in enumerate(heads):
+        g = kv_head(int(h), H, Hkv)
+        # the group's query heads with their one K/V head (grouped-query, H_kv = 1)
+        qs = np.asarray(q[b:b + 1, :, g * r:(g + 1) * r, :], np.float64)
+        dos = np.asarray(do[b:b + 1, :, g * r:(g + 1) * r, :], np.float64)
+        ks = np.asarray(k[b:b + 1, :, g:g + 1, :], np.float64)
+        vs = np.asarray(v[b:b + 1, :, g:g + 1, :], np.float64)
+        dq, dk, dv = attention_backward(qs, ks, vs, dos, scale, causal)
+        out[0][i] = dq[0, :, h - g * r, :]
+        out[1][i] = dk[0, :, 0, :]
+        out[2][i] = dv[0, :, 0, :]
     return tuple(out)

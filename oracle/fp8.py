@@ -192,7 +192,8 @@ def dequantize(codes, scales) -> np.ndarray:
 
 
 def fp8_attention_emulation(q8, k8, v8, sq, sk, sv, scale: float, causal: bool,
-                            Bc: int = QBLOCK, quantize_p: bool = True, rows=None):
+                            Bc: int = QBLOCK, quantize_p: bool = True, rows=None,
+                            observer=None):
     """FP8 attention forward as the FP8 path computes it, in fp64.
 
     Inputs are e4m3 codes (BSHD) and per-128-row block scales [B,H,ceil(N/128)];
@@ -206,6 +207,12 @@ def fp8_attention_emulation(q8, k8, v8, sq, sk, sv, scale: float, causal: bool,
       O   = exp(m - m') O + e4m3(P_j) (V8_j * sV_j)
     Returns (O, LSE) for all rows (O BSHD, LSE [B,H,N]) or, when ``rows``
     ([R,3] of (b,h,i)) is given, (O_rows [R,d], LSE_rows [R]).
+
+    observer: optional callable, called after each key block with
+    (b, h, g, qi_idx, keys, s, m_new, p, alpha): the K/V head g, the query
+    rows, the block's keys, its scores S_j, the running max m' after it, the
+    unrounded P block and the rescale factor exp(m - m').  It only watches
+    (the tests derive error bounds from it); the result does not depend on it.
     """
     qv, kv, vv = e4m3_decode(q8), e4m3_decode(k8), e4m3_decode(v8)
     B, N, H, d = qv.shape
@@ -238,6 +245,8 @@ def fp8_attention_emulation(q8, k8, v8, sq, sk, sv, scale: float, causal: bool,
             pq = e4m3_decode(e4m3_encode(p)) if quantize_p else p
             acc = alpha[:, None] * acc + pq @ (vv[b, c0:c1, g, :] * svc[:, None])
             m = m_new
+            if observer is not None:
+                observer(b, h, g, qi_idx, keys, s, m_new, p, alpha)
         return acc / l[:, None], m + np.log(l)
 
     if rows is not None:

@@ -5,7 +5,11 @@ emulation of the pre-pass (both take the quantise decision in fp32, with the
 same butterfly order).
 
 attn_fwd_fp8 (fed the oracle's own codes and scales):
-  * tight gate vs the oracle's FP8 emulation: RMSE(GPU - emulation) <= 0.1 x
+  * per element vs the oracle's FP8 emulation: |o_gpu - o_emul| within the
+    bound of tests/fp8_bound.py (bf16 output rounding, a possible one-step
+    e4m3 flip of each P lying within the fp32 error of a rounding midpoint,
+    fp32 accumulation slack), with the RMS of err/bound <= 0.45;
+  * tight norm gate vs the emulation: RMSE(GPU - emulation) <= 0.1 x
     RMSE(emulation - exact);
   * vs exact fp64 attention on the unrotated bf16 inputs: RMSE <= 3e-2 on the
     outlier distribution of the FlashAttention-3 report (section 4.3), and
@@ -19,6 +23,7 @@ import torch
 
 import oracle
 import workloads
+from fp8_bound import check_fp8, emulation_with_bound
 from gpu_helpers import DEV, err_stats, rows_of, say, to_np
 
 import exact_attention_74_amd as ea
@@ -108,8 +113,9 @@ def test_fp8_attention_vs_emulation_full(causal, d, N):
     signs = workloads.gen_signs(d)
     qs = _quant_all(q, k, v, signs, 128)
     o, lse = _gpu_fp8(*qs, w.softmax_scale, causal)
-    o_em, l_em = oracle.fp8_attention_emulation(*qs, w.softmax_scale, causal)
+    o_em, l_em, bound = emulation_with_bound(*qs, w.softmax_scale, causal)
     o_ex, l_ex = oracle.naive_attention(q, k, v, w.softmax_scale, causal)
+    check_fp8(o, o_em, bound, w.name)
     e_kernel = _rmse(o, o_em)
     e_scheme = _rmse(o_em, o_ex)
     lerr = float(np.abs(lse - l_em).max())
@@ -141,19 +147,21 @@ def test_fp8_full_size_rows_and_baseline(w):
 
     o_fa3 = gpu_path(ts, 128)
     o_base = gpu_path(None, 0)
-    got_fa3, got_base, ref_ex, ref_em = [], [], [], []
+    got_fa3, got_base, ref_ex, ref_em, bounds = [], [], [], [], []
     for b, h in ((0, 0), (1, 5), (2, 10), (3, 15)):
         sl = [x[b:b + 1, :, h:h + 1] for x in (q, k, v)]
         rows = workloads.sample_rows(1, 1, w.N, 128, seed=77 + h)
         o_ex, _ = oracle.naive_attention_rows(*sl, w.softmax_scale, False, rows)
-        o_em, _ = oracle.fp8_attention_emulation(*_quant_all(*sl, signs, 128), w.softmax_scale,
-                                                 False, rows=rows)
+        o_em, _, bd = emulation_with_bound(*_quant_all(*sl, signs, 128), w.softmax_scale, False,
+                                           rows=rows)
         i = rows[:, 2]
         got_fa3.append(o_fa3[b, i, h])
         got_base.append(o_base[b, i, h])
         ref_ex.append(o_ex)
         ref_em.append(o_em)
+        bounds.append(bd)
     o_fa3, o_base, o_ex, o_em = (np.concatenate(a) for a in (got_fa3, got_base, ref_ex, ref_em))
+    check_fp8(o_fa3, o_em, np.concatenate(bounds), w.name)
     e_fa3, e_base, e_em = _rmse(o_fa3, o_ex), _rmse(o_base, o_ex), _rmse(o_em, o_ex)
     e_kernel = _rmse(o_fa3, o_em)
     rel = e_fa3 / float(np.sqrt(np.mean(o_ex ** 2)))
@@ -173,6 +181,9 @@ def test_fp8_lse_vs_exact_normal_inputs():
     qs = _quant_all(q, k, v, workloads.gen_signs(128), 128)
     o, lse = _gpu_fp8(*qs, w.softmax_scale, False)
     o_ex, l_ex = oracle.naive_attention(q, k, v, w.softmax_scale, False)
+    rows = workloads.sample_rows(w.B, w.H, w.N, 256, seed=61)
+    o_em, _, bound = emulation_with_bound(*qs, w.softmax_scale, False, rows=rows)
+    check_fp8(rows_of(o, rows), o_em, bound, w.name)
     mx, rmse = err_stats(o, o_ex)
     print(f"fp8 normal: max={mx:.3e} rmse={rmse:.3e} lse={np.abs(lse - l_ex).max():.3e}")
     assert rmse <= 3e-3 and np.abs(lse - l_ex).max() <= 5e-2
@@ -196,20 +207,22 @@ def test_fp8_d256_full_size_sampled_rows(causal):
     o, lse = ea.attn_fwd_fp8(q8, k8, v8, sq, sk, sv, causal=causal, softmax_scale=w.softmax_scale)
     torch.cuda.synchronize()
     o, lse = to_np(o), lse.cpu().numpy().astype(np.float64)
-    got, ref_ex, ref_em, l_got, l_em = [], [], [], [], []
+    got, ref_ex, ref_em, l_got, l_em, bounds = [], [], [], [], [], []
     for b, h in ((0, 0), (1, 3), (1, 7)):
         sl = [x[b:b + 1, :, h:h + 1] for x in (q, k, v)]
         rows = workloads.sample_rows(1, 1, w.N, 128, seed=91 + h)
         o_ex, _ = oracle.naive_attention_rows(*sl, w.softmax_scale, causal, rows)
-        o_em, le = oracle.fp8_attention_emulation(*_quant_all(*sl, signs, 128), w.softmax_scale,
-                                                  causal, rows=rows)
+        o_em, le, bd = emulation_with_bound(*_quant_all(*sl, signs, 128), w.softmax_scale,
+                                            causal, rows=rows)
         i = rows[:, 2]
         got.append(o[b, i, h])
         l_got.append(lse[b, h, i])
         ref_ex.append(o_ex)
         ref_em.append(o_em)
         l_em.append(le)
+        bounds.append(bd)
     o, o_ex, o_em = (np.concatenate(a) for a in (got, ref_ex, ref_em))
+    check_fp8(o, o_em, np.concatenate(bounds), w.name)
     e_kernel, e_em, e_ex = _rmse(o, o_em), _rmse(o_em, o_ex), _rmse(o, o_ex)
     lerr = float(np.abs(np.concatenate(l_got) - np.concatenate(l_em)).max())
     print(f"{w.name}: rmse gpu-vs-emulation={e_kernel:.3e} emulation floor={e_em:.3e} "
@@ -237,9 +250,10 @@ def test_fp8_causal_schedules_sampled_rows(B, H, N, d):
     o2, lse2 = _gpu_fp8(*qs, w.softmax_scale, True)
     assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
     rows = workloads.sample_rows(B, H, N, 384, seed=N + 3)
-    o_em, l_em = oracle.fp8_attention_emulation(*qs, w.softmax_scale, True, rows=rows)
+    o_em, l_em, bound = emulation_with_bound(*qs, w.softmax_scale, True, rows=rows)
     o_ex, _ = oracle.naive_attention_rows(q, k, v, w.softmax_scale, True, rows)
     got = rows_of(o, rows)
+    check_fp8(got, o_em, bound, w.name)
     e_kernel, e_scheme = _rmse(got, o_em), _rmse(o_em, o_ex)
     lerr = float(np.abs(lse[rows[:, 0], rows[:, 1], rows[:, 2]] - l_em).max())
     print(f"{w.name}: rmse(gpu-emul)={e_kernel:.3e} rmse(emul-exact)={e_scheme:.3e} "

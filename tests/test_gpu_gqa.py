@@ -12,6 +12,7 @@ import torch
 
 import oracle
 import workloads
+from fp8_bound import check_fp8, emulation_with_bound
 from gpu_helpers import DEV, err_stats, lse_rows, rows_of, say, to_np
 
 import exact_attention_74_amd as ea
@@ -118,8 +119,9 @@ def test_fp8_gqa_vs_emulation(N, d, H, Hkv, causal):
     o, lse = ea.attn_fwd_fp8_gqa(*t, causal=causal, softmax_scale=scale)
     torch.cuda.synchronize()
     o, lse = to_np(o), lse.cpu().numpy().astype(np.float64)
-    o_em, l_em = oracle.fp8_attention_emulation(q8, k8, v8, sq, sk, sv, scale, causal)
+    o_em, l_em, bound = emulation_with_bound(q8, k8, v8, sq, sk, sv, scale, causal)
     o_ex, _ = oracle.naive_attention(q, k, v, scale, causal)
+    check_fp8(o, o_em, bound, tag)
     e_kernel, e_scheme = _rmse(o, o_em), _rmse(o_em, o_ex)
     lerr = float(np.abs(lse - l_em).max())
     print(f"{tag}: rmse(gpu-emul)={e_kernel:.3e} rmse(emul-exact)={e_scheme:.3e} "

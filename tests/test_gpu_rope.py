@@ -13,6 +13,7 @@ import torch
 
 import oracle
 import workloads
+from fp8_bound import check_fp8, emulation_with_bound
 from gpu_helpers import DEV, say, to_np
 
 import exact_attention_74_amd as ea
@@ -88,7 +89,8 @@ def test_rope_fp8_attention_end_to_end(causal):
     qc, qs = oracle.blockquant_hadamard(oracle.rope_fp32(q, cos, sin, False), signs, 128)
     kc, ks = oracle.blockquant_hadamard(oracle.rope_fp32(k, cos, sin, False), signs, 128)
     vc, vs = oracle.blockquant_hadamard(v, None, 128)
-    o_em, _ = oracle.fp8_attention_emulation(qc, kc, vc, qs, ks, vs, scale, causal)
+    o_em, _, bound = emulation_with_bound(qc, kc, vc, qs, ks, vs, scale, causal)
+    check_fp8(o, o_em, bound, f"rope fp8 causal={causal}")
     rmse = float(np.sqrt(np.mean((o - o_ex) ** 2)))
     e_kernel = float(np.sqrt(np.mean((o - o_em) ** 2)))
     e_scheme = float(np.sqrt(np.mean((o_em - o_ex) ** 2)))

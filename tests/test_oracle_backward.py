@@ -109,3 +109,22 @@ def test_gqa_matches_torch_autograd(H, Hkv, causal):
     ref = _torch_grads_gqa(q, k, v, do, 0.3, causal)
     for g, r in zip(got, ref):
         np.testing.assert_allclose(g, r, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 2), (6, 1), (8, 4)])
+def test_heads_variant_grouped_query(H, Hkv):
+    """For grouped-query inputs the per-head helper returns dQ of the query
+    head and dK, dV of the K/V head it reads (the group sums), equal to the
+    full oracle's; torch autograd pins the full oracle for these shapes."""
+    q, do = _rand((2, 33, H, 8), 25), _rand((2, 33, H, 8), 26)
+    k, v = _rand((2, 33, Hkv, 8), 27), _rand((2, 33, Hkv, 8), 28)
+    full = attention_backward(q, k, v, do, 0.45, True)
+    heads = np.array([[0, H - 1], [1, 0], [1, H // 2]])
+    part = attention_backward_heads(q, k, v, do, 0.45, True, heads)
+    r = H // Hkv
+    for i, (b, h) in enumerate(heads):
+        np.testing.assert_allclose(part[0][i], full[0][b, :, h, :], rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(part[1][i], full[1][b, :, h // r, :], rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(part[2][i], full[2][b, :, h // r, :], rtol=1e-13, atol=1e-14)
+    ref = _torch_grads_gqa(q, k, v, do, 0.45, True)
+    np.testing.assert_allclose(part[1][0], ref[1][0, :, (H - 1) // r, :], rtol=1e-10, atol=1e-12)

@@ -238,6 +238,46 @@ def test_emulation_exact_when_p_is_representable(causal):
     np.testing.assert_allclose(l, l_ref, rtol=1e-12, atol=1e-13)
 
 
+def test_emulation_rounds_p_against_the_running_max():
+    """The FP8 path rounds P_j = exp(S_j - m_j) to e4m3 with m_j the running
+    row max after key block j ([FA3-report] section 3: the online softmax
+    never sees the final max while block j is processed).
+
+    Two key blocks (N = 129, blocks of 128): block 0 holds the scores ln2 * n
+    (n integer in [-6, 0], max 0); the ragged block 1 holds one key of score
+    ln 3, so the row max rises by ln 3 after block 0.  Against the running max
+    every P is a power of two (2^n, then 1), exact in e4m3, so the emulation
+    equals exact attention on the dequantised operands.  Rounding block 0's P
+    against the final max instead (2^n / 3, between e4m3 values) moves the
+    output by a few per cent of an e4m3 step; the same check, written for that
+    reading here, fails by far more than the tolerance."""
+    B, N, H, d = 1, 129, 1, 16
+    one = e4m3_encode(1.0)
+    q8 = np.zeros((B, N, H, d), np.uint8)
+    q8[..., 0] = one
+    n = -np.random.default_rng(11).integers(0, 7, size=128)
+    n[5] = 0
+    k8 = np.zeros((B, N, H, d), np.uint8)
+    k8[0, :128, 0, 0] = e4m3_encode(n.astype(np.float64))
+    k8[0, 128, 0, 0] = one
+    v8 = _random_codes((B, N, H, d), 12)
+    sq = np.ones((B, H, 2), np.float32)
+    sk = np.array([[[math.log(2.0), math.log(3.0)]]], np.float32)
+    sv = np.ones((B, H, 2), np.float32)
+    o, lse = fp8_attention_emulation(q8, k8, v8, sq, sk, sv, 1.0, False)
+    qd, kd, vd = dequantize(q8, sq), dequantize(k8, sk), dequantize(v8, sv)
+    o_ref, l_ref = naive_attention(qd, kd, vd, 1.0, False)
+    # fl32(ln 2) makes each P of block 0 2^n (1 + O(1e-7)): exact after rounding
+    np.testing.assert_allclose(o, o_ref, rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(lse, l_ref, rtol=1e-12, atol=1e-12)
+    # the final-max reading on the same operands
+    s = (qd[0, :, 0] @ kd[0, :, 0].T)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    o_final = (e4m3_decode(e4m3_encode(p)) @ vd[0, :, 0]) / p.sum(axis=1, keepdims=True)
+    assert np.abs(o_final - o_ref[0, :, 0]).max() > 1e-3 * np.abs(o_ref).max()
+    assert np.abs(o_final - o[0, :, 0]).max() > 100 * np.abs(o - o_ref).max()
+
+
 def test_emulation_rows_variant():
     q8, k8, v8 = (_random_codes((2, 200, 2, 32), s) for s in (7, 8, 9))
     sc = np.full((2, 2, 2), 0.01, np.float32)
