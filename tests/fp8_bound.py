@@ -7,15 +7,18 @@ only by:
 
   1. O rounded to bf16 at the end:                <= 2^-8 |O|.
   2. P_gpu = P_emul (1 + eta) before the e4m3 rounding, with eta bounded from
-     the fp32 arithmetic of each score (MFMA accumulation over d products of
-     e4m3 codes, the tile's scale product, the running max, the fused
-     multiply-add and exp2).  Where P_emul lies within eta of a rounding
+     the arithmetic of each score: the e4m3 MFMA's dot product (on gfx950 its
+     result is not the fp32-rounded exact sum: it deviates by up to 2^-14.9 of
+     sum |q_k k_k| in a probe of 64-wide k-steps; EPS_MFMA = 2^-13 is taken,
+     and tests/test_gpu_mfma_precision.py checks it on the device), the
+     tile's scale product, the running max, the fused multiply-add and exp2.  Where P_emul lies within eta of a rounding
      midpoint the two roundings may pick neighbouring e4m3 values: a change of
      one e4m3 spacing in that P, times |V| sv, over l.
-  3. fp32 accumulation of O and l over the keys, the per-tile rescale
-     factors (exp2 of the max difference, the V-scale ratio by reciprocal)
-     and the final division: relative slack kappa on sum P|V|sv / l, and
-     kappa_l (including the largest eta, which moves l) on |O|.
+  3. The P.V MFMA (the same EPS_MFMA of sum P|V| per k-step), fp32
+     accumulation of O and l over the keys, the per-tile rescale factors
+     (exp2 of the max difference, the V-scale ratio by reciprocal) and the
+     final division: relative slack kappa on sum P|V|sv / l, and kappa_l
+     (including the largest eta, which moves l) on |O|.
 
 Test infrastructure: reads the oracle's emulation through its observer hook
 and adds no arithmetic to it.
@@ -30,6 +33,7 @@ import oracle
 
 U_BF16 = 2.0 ** -8
 U32 = 2.0 ** -23          # one fp32 rounding, allowing truncation
+EPS_MFMA = 2.0 ** -13     # e4m3 MFMA dot product: |error| <= EPS_MFMA sum |a_k b_k|
 LOG2E = 1.0 / math.log(2.0)
 _MAGS = np.sort(oracle.e4m3_decode_table()[:127])  # non-negative e4m3 values, 0 .. 448
 
@@ -64,7 +68,7 @@ def emulation_with_bound(q8, k8, v8, sq, sk, sv, scale: float, causal: bool, row
         qk_abs = np.abs(qv[b, qi, h, :]) @ np.abs(kv[b, keys, g, :]).T
         t = np.where(vis, s, 0.0) * LOG2E
         mm = (m_new * LOG2E)[:, None]
-        dx = c * d * U32 * qk_abs + (np.abs(t) + np.abs(mm)) * 4 * U32 + np.abs(t - mm) * U32
+        dx = c * EPS_MFMA * qk_abs + (np.abs(t) + np.abs(mm)) * 4 * U32 + np.abs(t - mm) * U32
         eta = np.where(vis, math.log(2.0) * dx + 2 * U32, 0.0)
         step = e4m3_flip_step(p, eta)
         pq = oracle.e4m3_decode(oracle.e4m3_encode(p))
@@ -90,7 +94,7 @@ def emulation_with_bound(q8, k8, v8, sq, sk, sv, scale: float, causal: bool, row
         rows = np.asarray(rows, np.int64)
         where = {(int(b), int(h), int(i)): r for r, (b, h, i) in enumerate(rows)}
     for (b, h, _, _), st in state.items():
-        kappa = (st["nk"] + 4 * st["nb"] + 16) * U32 + st["dalpha"]
+        kappa = EPS_MFMA + (st["nk"] + 4 * st["nb"] + 16) * U32 + st["dalpha"]
         kappa_l = st["eta"] + (st["nk"] + 4 * st["nb"] + 8) * U32 + st["dalpha"]
         l = st["l"][:, None]
         for j, i in enumerate(st["qi"]):
