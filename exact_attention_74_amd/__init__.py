@@ -39,6 +39,7 @@ SIGNATURES = {
     "attn_bwd_bf16": [_c_void_p] * 10 + [_c_int] * 5 + [_c_float, _c_void_p],
     "attn_bwd_bf16_gqa": [_c_void_p] * 10 + [_c_int] * 6 + [_c_float, _c_void_p],
     "attn_bwd_bf16_workspace_bytes": [_c_int] * 3,
+    "attn_bwd_bf16_noalloc": [_c_void_p] * 9 + [_c_int] * 6 + [_c_float, _c_void_p],
     "rope_blockquant_hadamard": [_c_void_p] * 6 + [_c_int] * 6 + [_c_void_p],
     "blockquant_hadamard": [_c_void_p] * 4 + [_c_int] * 5 + [_c_void_p],
     "exattn_strerror": [_c_int],
@@ -46,7 +47,8 @@ SIGNATURES = {
 }
 RESTYPES = {"exattn_strerror": ctypes.c_char_p, "attn_bwd_bf16_workspace_bytes": ctypes.c_longlong}
 
-ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_VALUE, ERR_HIP = -1, -2, -3, -4, -5
+ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_VALUE, ERR_HIP, ERR_SCRATCH = -1, -2, -3, -4, -5, -6
+NOALLOC_SCRATCH_BYTES = 16 << 20  # EXATTN_NOALLOC_SCRATCH_BYTES
 
 # torch device type that every tensor argument must have (HIP devices appear
 # as "cuda" in PyTorch-ROCm)
@@ -307,6 +309,34 @@ def attn_bwd_bf16(q, k, v, o, lse, do, causal: bool = False, softmax_scale: floa
     return dq, dk, dv
 
 
+def attn_bwd_bf16_noalloc(q, k, v, o, lse, do, dq, dk, dv, causal: bool = False,
+                          softmax_scale: float | None = None):
+    """attn_bwd_bf16 into caller-supplied dq, dk, dv with no device allocation
+    at all (the per-row workspace lives in the library's fixed per-GPU
+    scratch; 8 B H N must be <= NOALLOC_SCRATCH_BYTES).  Calls overlapping on
+    one GPU race on that scratch.  Returns (dq, dk, dv)."""
+    shape = _check_bshd("q", q, torch.bfloat16)
+    for name, t in (("o", o), ("do", do)):
+        if _check_bshd(name, t, torch.bfloat16) != shape:
+            raise ValueError(f"{name} must have q's shape")
+    Hkv = _kv_heads("attn_bwd_bf16", shape, _check_bshd("k", k, torch.bfloat16),
+                    _check_bshd("v", v, torch.bfloat16), grouped=True)
+    B, N, H, d = shape
+    for name, t in (("k", k), ("v", v), ("o", o), ("do", do)):
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on q's device")
+    _check_out("lse", lse, (B, H, N), torch.float32, q.device)
+    _check_out("dq", dq, (B, N, H, d), torch.bfloat16, q.device)
+    _check_out("dk", dk, tuple(k.shape), torch.bfloat16, q.device)
+    _check_out("dv", dv, tuple(v.shape), torch.bfloat16, q.device)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    _call("attn_bwd_bf16_noalloc", q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+          do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv,
+          N, d, int(bool(causal)), scale, _stream_ptr(q))
+    return dq, dk, dv
+
+
 __all__ = ["attn_fwd_bf16", "attn_fwd_fp8", "attn_fwd_bf16_gqa", "attn_fwd_fp8_gqa", "attn_bwd_bf16",
+           "attn_bwd_bf16_noalloc",
            "blockquant_hadamard", "rope_blockquant_hadamard", "lib", "strerror",
            "ExattnError", "LIB_PATH", "SIGNATURES"]

@@ -67,7 +67,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? EXATTN_OK : EXATTN_ERR_H
 
 extern "C" {
 
-int exattn_abi_version(void) { return 6; }
+int exattn_abi_version(void) { return 7; }
 
 const char* exattn_strerror(int code) {
   switch (code) {
@@ -81,6 +81,9 @@ const char* exattn_strerror(int code) {
       return "invalid value (softmax_scale, causal, block_rows, or an output overlapping an "
              "input or another output)";
     case EXATTN_ERR_HIP: return "HIP error (no device or kernel launch failed)";
+    case EXATTN_ERR_SCRATCH:
+      return "problem too large for the fixed scratch of the no-allocation entry point "
+             "(8 B H N bytes above EXATTN_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown error code";
   }
 }
@@ -178,6 +181,33 @@ int attn_bwd_bf16_gqa(const void* q, const void* k, const void* v, const void* o
   return hip_status(exattn::launch_attn_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, workspace, B,
                                                  H, H_kv, N, d, causal != 0, softmax_scale,
                                                  (hipStream_t)stream));
+}
+
+int attn_bwd_bf16_noalloc(const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                          int H, int H_kv, int N, int d, int causal, float softmax_scale,
+                          void* stream) {
+  int rc = check_shape(B, H, N, d, 2, /*allow_d256=*/false);
+  if (rc) return rc;
+  if (!good_heads(H, H_kv)) return EXATTN_ERR_SHAPE;
+  if ((causal != 0 && causal != 1) || !good_scale(softmax_scale)) return EXATTN_ERR_VALUE;
+  if ((int64_t)8 * B * H * N > (int64_t)exattn::bwd_scratch_bytes()) return EXATTN_ERR_SCRATCH;
+  const int64_t bytes = (int64_t)B * N * H * d * 2;
+  if (bytes == 0) return EXATTN_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return EXATTN_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4))
+    return EXATTN_ERR_ALIGN;
+  const int64_t lse_bytes = (int64_t)B * H * N * 4;
+  const int64_t kv_bytes = (int64_t)B * N * H_kv * d * 2;
+  if (aliased({{dq, bytes}, {dk, kv_bytes}, {dv, kv_bytes}},
+              {{q, bytes}, {k, kv_bytes}, {v, kv_bytes}, {o, bytes}, {dout, bytes},
+               {lse, lse_bytes}}))
+    return EXATTN_ERR_VALUE;
+  return hip_status(exattn::launch_attn_bwd_bf16_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H,
+                                                         H_kv, N, d, causal != 0, softmax_scale,
+                                                         (hipStream_t)stream));
 }
 
 int attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -32,7 +32,10 @@
 // that is read both row-wise (ds_read_b128, an A operand) and transposed
 // (ds_read_b64_tr_b16) uses the chunk swizzle swz_b, free of bank conflicts
 // for both patterns.
+#include <mutex>
+
 #include "common.h"
+#include "exattn.h"
 #include "launch.h"
 #include "lds_tile.h"
 
@@ -500,7 +503,45 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   return hipGetLastError();
 }
 
+// Fixed device scratch for callers that cannot allocate (the no-allocation
+// gradient entry point): it takes the place of the caller's workspace (D and
+// LSE * log2(e), 8 B H N bytes).  One copy per GPU, resident until the
+// process ends; its device address is looked up once per device.
+constexpr size_t kScratchBytes = EXATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+float* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_status[kMaxDevices];
+
 }  // namespace
+
+size_t bwd_scratch_bytes() { return kScratchBytes; }
+
+hipError_t launch_attn_bwd_bf16_noalloc(const void* q, const void* k, const void* v,
+                                        const void* o, const void* dout, const float* lse,
+                                        void* dq, void* dk, void* dv, int B, int H, int Hkv,
+                                        int N, int d, bool causal, float softmax_scale,
+                                        hipStream_t stream) {
+  if ((size_t)8 * B * H * N > kScratchBytes) return hipErrorInvalidValue;  // checked by the caller
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  // The symbol's device address, taken with this device current (each GPU
+  // holds its own copy of the array); the host-side name is not a device
+  // address and is never passed to a kernel.
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    g_scratch_status[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = static_cast<float*>(ptr);
+  });
+  if (g_scratch_status[dev] != hipSuccess) return g_scratch_status[dev];
+  if (g_scratch_ptr[dev] == nullptr) return hipErrorInvalidSymbol;
+  return launch_attn_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, g_scratch_ptr[dev], B, H, Hkv, N,
+                              d, causal, softmax_scale, stream);
+}
 
 hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                                 const void* dout, const float* lse, void* dq, void* dk, void* dv,

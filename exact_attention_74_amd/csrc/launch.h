@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <stddef.h>
+
 #include <atomic>
 
 namespace exattn {
@@ -58,6 +60,15 @@ hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
                                 const void* dout, const float* lse, void* dq, void* dk, void* dv,
                                 float* workspace, int B, int H, int Hkv, int N, int d,
                                 bool causal, float softmax_scale, hipStream_t stream);
+
+// The same with the workspace in the library's fixed per-device scratch
+// array (bwd_scratch_bytes() bytes; 8 B H N must fit): no allocation.
+hipError_t launch_attn_bwd_bf16_noalloc(const void* q, const void* k, const void* v,
+                                        const void* o, const void* dout, const float* lse,
+                                        void* dq, void* dk, void* dv, int B, int H, int Hkv,
+                                        int N, int d, bool causal, float softmax_scale,
+                                        hipStream_t stream);
+size_t bwd_scratch_bytes();
 
 hipError_t launch_blockquant(const void* x, void* x8, float* scale, const float* signs, int B, int H,
                              int N, int d, int block_rows, hipStream_t stream);

@@ -63,6 +63,10 @@ extern "C" {
 #define EXATTN_ERR_ALIGN (-3) /* a pointer is not aligned as required             */
 #define EXATTN_ERR_VALUE (-4) /* bad softmax_scale/causal/block_rows, or aliasing */
 #define EXATTN_ERR_HIP (-5)   /* no HIP device, or a launch failed                */
+#define EXATTN_ERR_SCRATCH (-6) /* too large for attn_bwd_bf16_noalloc's scratch */
+
+/* Bytes of the fixed per-GPU scratch array behind attn_bwd_bf16_noalloc. */
+#define EXATTN_NOALLOC_SCRATCH_BYTES (16 << 20)
 
 /*
  * bf16 attention forward.
@@ -146,6 +150,25 @@ int attn_bwd_bf16_gqa(const void* q, const void* k, const void* v, const void* o
                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
                       float* workspace, int B, int H, int H_kv, int N, int d, int causal,
                       float softmax_scale, void* stream);
+
+/*
+ * attn_bwd_bf16_gqa without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Arguments, outputs and results are those
+ * of attn_bwd_bf16_gqa (H_kv = H for plain multi-head attention); the
+ * per-row D and LSE*log2(e) go to a fixed scratch array of
+ * EXATTN_NOALLOC_SCRATCH_BYTES bytes held by the library on each GPU until
+ * the process ends, so 8 * B * H * N must not exceed it (EXATTN_ERR_SCRATCH
+ * otherwise, before any HIP call).  The call allocates nothing.  Every call
+ * on one GPU uses that GPU's one scratch array: calls that overlap in time on
+ * the same GPU (other streams, other host threads) race and must be
+ * serialised by the caller.  The scratch is fully rewritten by each call
+ * before it is read, so nothing needs clearing between calls.
+ */
+int attn_bwd_bf16_noalloc(const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                          int B, int H, int H_kv, int N, int d, int causal, float softmax_scale,
+                          void* stream);
 
 /*
  * FP8 pre-pass: optional incoherent rotation, then block quantisation to e4m3

@@ -31,13 +31,14 @@ def _codes():
 
 def test_library_builds_and_loads():
     assert os.path.exists(ea.LIB_PATH)
-    assert ea.lib().exattn_abi_version() == 6
+    assert ea.lib().exattn_abi_version() == 7
 
 
 def test_exports_every_declared_symbol():
     names = _declared()
     assert set(names) == {"attn_fwd_bf16", "attn_fwd_fp8", "attn_fwd_bf16_gqa", "attn_fwd_fp8_gqa",
                           "attn_bwd_bf16", "attn_bwd_bf16_gqa", "attn_bwd_bf16_workspace_bytes",
+                          "attn_bwd_bf16_noalloc",
                           "rope_blockquant_hadamard",
                           "blockquant_hadamard", "exattn_strerror", "exattn_abi_version"}
     raw = ctypes.CDLL(ea.LIB_PATH)
@@ -50,9 +51,11 @@ def test_error_codes_match_header():
     c = _codes()
     assert c["EXATTN_OK"] == 0
     assert (c["EXATTN_ERR_NULL"], c["EXATTN_ERR_SHAPE"], c["EXATTN_ERR_ALIGN"],
-            c["EXATTN_ERR_VALUE"], c["EXATTN_ERR_HIP"]) == (ea.ERR_NULL, ea.ERR_SHAPE, ea.ERR_ALIGN,
-                                                           ea.ERR_VALUE, ea.ERR_HIP)
-    for code in (0, -1, -2, -3, -4, -5):
+            c["EXATTN_ERR_VALUE"], c["EXATTN_ERR_HIP"], c["EXATTN_ERR_SCRATCH"]) == (
+                ea.ERR_NULL, ea.ERR_SHAPE, ea.ERR_ALIGN, ea.ERR_VALUE, ea.ERR_HIP, ea.ERR_SCRATCH)
+    text = open(HEADER).read()
+    assert f"EXATTN_NOALLOC_SCRATCH_BYTES ({ea.NOALLOC_SCRATCH_BYTES >> 20} << 20)" in text
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert ea.strerror(code) and ea.strerror(code) != "unknown error code"
     assert ea.strerror(-99) == "unknown error code"
 
@@ -227,3 +230,30 @@ def test_aliasing_every_output_input_pair():
     # backward: lse input against the workspace and gradients
     assert _bwd(dv=P + 5 * P2 + 16) == ea.ERR_VALUE       # dV over the LSE
 
+
+
+def _bwd_na(q=P, k=P + P2, v=P + 2 * P2, o=P + 3 * P2, do=P + 4 * P2, lse=P + 5 * P2,
+            dq=P + 6 * P2, dk=P + 7 * P2, dv=P + 8 * P2, B=1, H=2, Hkv=2, N=256, d=64, causal=0,
+            scale=0.125):
+    return ea.lib().attn_bwd_bf16_noalloc(q, k, v, o, do, lse, dq, dk, dv, B, H, Hkv, N, d,
+                                          causal, scale, None)
+
+
+def test_bwd_noalloc_validation():
+    """The no-allocation gradient entry point validates like attn_bwd_bf16_gqa
+    and rejects problems whose per-row workspace (8 B H N bytes) exceeds its
+    fixed scratch, before any HIP call."""
+    cap = ea.NOALLOC_SCRATCH_BYTES
+    assert _bwd_na(N=cap // 16 + 1) == ea.ERR_SCRATCH            # 8 * 1 * 2 * N > cap
+    assert _bwd_na(B=4, H=8, Hkv=8, N=cap // 256 + 64) == ea.ERR_SCRATCH
+    assert _bwd_na(N=cap // 16, q=None) == ea.ERR_NULL            # exactly at the limit: fits
+    for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"):
+        assert _bwd_na(**{name: None}) == ea.ERR_NULL, name
+    assert _bwd_na(d=256) == ea.ERR_SHAPE
+    assert _bwd_na(Hkv=3) == ea.ERR_SHAPE
+    assert _bwd_na(scale=0.0) == ea.ERR_VALUE
+    assert _bwd_na(dq=P + 6 * P2 + 8) == ea.ERR_ALIGN
+    assert _bwd_na(dq=P + 64) == ea.ERR_VALUE                     # dQ overlaps q
+    assert _bwd_na(dv=P + 7 * P2 + 64) == ea.ERR_VALUE            # dV overlaps dK
+    assert _bwd_na(B=0) == 0
+    assert ea.strerror(ea.ERR_SCRATCH).startswith("problem too large")
