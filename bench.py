@@ -14,9 +14,12 @@ median event time), with the fp8 figure and the pre-pass GB/s beside it.
 
 After the timed steps, further legs are timed the same way, each on its own
 launches: the bf16 gradients, the RoPE-fused pre-pass, the causal forwards,
-the head-dim-256 forwards and the bf16 forward on B2 H32 N4096, and (unless
---no-cpu-baseline) the fp64 CPU oracle on a bounded sample of the bf16
-workload.  Prints ONE JSON line.
+the head-dim-256 forwards, the bf16 forward on B2 H32 N4096, the GFX clock
+during the two headline forwards, the 16384-token sweep (36 configurations),
+the long single request B1 H8 N32768 causal, the FP8 accuracy figures with the
+2 x 2 ablation of block scales and rotation, and (unless --no-cpu-baseline)
+the fp64 CPU oracle on a bounded sample of the bf16 workload.  Prints ONE
+JSON line.
 """
 from __future__ import annotations
 
@@ -26,6 +29,8 @@ import math
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -63,6 +68,17 @@ def parse():
     p.add_argument("--c2-reps", type=int, default=20,
                    help="launches of the bf16 forward on B2 H32 N4096 d128, non-causal and causal "
                         "(0: skip)")
+    p.add_argument("--sweep-reps", type=int, default=10,
+                   help="launches per configuration of the 16384-token bf16 sweep (N 512..16k x "
+                        "d 64/96/128 x both masks; 0: skip)")
+    p.add_argument("--long-reps", type=int, default=10,
+                   help="launches of the long single-request forward B1 H8 N32768 d128 causal "
+                        "(0: skip)")
+    p.add_argument("--sclk-seconds", type=float, default=1.0,
+                   help="seconds of back-to-back launches per kernel while the GFX clock is "
+                        "sampled (0: skip)")
+    p.add_argument("--no-fp8-accuracy", action="store_true",
+                   help="skip the FP8 accuracy / ablation figures")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run one plain 256 MiB device copy (untimed), the reference that "
                         "scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -104,22 +120,23 @@ def cpu_baseline(w, target_s: float):
         threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
     rng = np.random.default_rng(w.seed)
     heads = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < target_s and heads < w.B * w.H:
+    el = 0.0  # oracle time only; each head's inputs are drawn before its timer starts
+    while el < target_s and heads < w.B * w.H:
         q, k, v = (workloads.to_bf16_f32(rng.standard_normal((1, w.N, 1, w.d), dtype=np.float32))
                    for _ in range(3))
         t1 = time.perf_counter()
         oracle.naive_attention(q, k, v, w.softmax_scale, w.causal, row_chunk=1024)
+        dt = time.perf_counter() - t1
+        el += dt
         heads += 1
         if heads == 1:
-            first = time.perf_counter() - t1
-    el = time.perf_counter() - t0
+            first = dt
     flops = 4.0 * heads * w.N * w.N * w.d / (2 if w.causal else 1)
     return {
         "value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
         "sample": f"{heads} of {w.B * w.H} (b,h) heads of N={w.N} d={w.d}"
-                  f"{' causal' if w.causal else ''}, fp64 numpy naive attention, {el:.1f} s "
-                  f"(first head {first:.1f} s); input generation included",
+                  f"{' causal' if w.causal else ''}, fp64 numpy naive attention, {el:.1f} s of "
+                  f"oracle time (first head {first:.1f} s); input generation not timed",
         "host_cpus": os.cpu_count(),
         "affinity_cpus": len(os.sched_getaffinity(0)),
     }
@@ -140,6 +157,80 @@ def time_reps(fn, reps: int, stream) -> float:
         e1.record(stream)
     torch.cuda.synchronize()
     return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e-3
+
+
+class ClockSampler:
+    """GFX (shader) clock of one GPU, sampled from amd-smi's metrics table by a
+    host thread (mean of the per-XCD current clocks, about every 2 ms) while
+    the main thread keeps the GPU busy."""
+
+    def __init__(self, dev):
+        import amdsmi
+        import torch
+        self._smi = amdsmi
+        amdsmi.amdsmi_init()
+        p = torch.cuda.get_device_properties(dev)
+        want = (int(p.pci_domain_id), int(p.pci_bus_id), int(p.pci_device_id))
+        self.handle = None
+        for hnd in amdsmi.amdsmi_get_processor_handles():
+            bdf = amdsmi.amdsmi_get_gpu_device_bdf(hnd)  # "dddd:bb:dd.f"
+            dom, bus, rest = bdf.split(":")
+            if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                self.handle = hnd
+        if self.handle is None:
+            raise RuntimeError(f"no amd-smi device at PCI {want}")
+
+    def _read(self):
+        m = self._smi.amdsmi_get_gpu_metrics_info(self.handle)
+        xs = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and c > 0]
+        if xs:
+            return float(sum(xs)) / len(xs)
+        c = m.get("current_gfxclk")
+        return float(c) if isinstance(c, (int, float)) else None
+
+    def measure(self, fn, seconds: float, stream):
+        """Mean MHz and sample count while ``fn`` is launched back to back for
+        about ``seconds`` (the first 20% of the samples, while the clock
+        settles, are dropped)."""
+        import threading
+        import torch
+        samples, stop = [], threading.Event()
+
+        def poll():
+            while not stop.is_set():
+                v = self._read()
+                if v is not None:
+                    samples.append(v)
+                time.sleep(0.002)
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        th = threading.Thread(target=poll, daemon=True)
+        th.start()
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(10):
+                fn()
+            n += 10
+            stream.synchronize()
+        stop.set()
+        th.join()
+        kept = samples[len(samples) // 5:]
+        return (float(np.mean(kept)) if kept else None), len(kept), n
+
+
+def fp64_rows_reference(q, k, v, b, h, rows, scale):
+    """Exact softmax attention (fp64, on the device) of the query rows ``rows``
+    of head (b, h); q, k, v bf16 BSHD device tensors.  Used for the accuracy
+    figures of the bench, which do not load the CPU oracle."""
+    import torch
+    idx = torch.as_tensor(rows, device=q.device)
+    qr = q[b, idx, h].double()
+    kh, vh = k[b, :, h].double().contiguous(), v[b, :, h].double().contiguous()
+    s = (qr @ kh.T) * scale
+    p = torch.softmax(s, dim=1)
+    return p @ vh
 
 
 def main():
@@ -381,6 +472,125 @@ def main():
         res["finite"] = bool(torch.isfinite(oc2).all().item())
         out["b2h32n4096"] = res
         del xc2, oc2, lc2
+    if a.sclk_seconds > 0:
+        # GFX clock while each headline kernel runs back to back: the fraction
+        # of the published peak (quoted at 2.4 GHz) that the achieved rate
+        # reaches at the clock the chip actually ran at.
+        print("[bench] gfx clock during the bf16 and fp8 forwards", file=sys.stderr, flush=True)
+        try:
+            cs = ClockSampler(dev)
+            res = {"source": "amd-smi gpu_metrics current_gfxclks (mean over the XCDs), sampled "
+                             "every ~2 ms by a host thread during back-to-back launches",
+                   "peak_clock_mhz": 2400.0}
+            for name, fn, tf, peak in (
+                    ("attn_fwd_bf16", lambda: ea.attn_fwd_bf16(q, k, v, causal=a.causal,
+                                                               softmax_scale=scale, out=o16,
+                                                               lse=lse16), tf16, PEAK_BF16_TFLOPS),
+                    ("attn_fwd_fp8", lambda: ea.attn_fwd_fp8(codes[0], codes[1], codes[2],
+                                                             *scales, causal=a.causal,
+                                                             softmax_scale=scale, out=o8,
+                                                             lse=lse8), tf8, PEAK_FP8_TFLOPS)):
+                mhz, n, launches = cs.measure(fn, a.sclk_seconds, stream)
+                res[name] = {"mhz": None if mhz is None else round(mhz, 1), "samples": n,
+                             "launches": launches,
+                             "frac_of_peak_at_this_clock": None if not mhz else
+                             round(tf / (peak * mhz / 2400.0), 4)}
+            out["sclk"] = res
+        except Exception as e:  # the clock is context; the bench goes on without it
+            out["sclk"] = {"error": f"{type(e).__name__}: {e}"}
+    if a.sweep_reps > 0 and a.d == 128:
+        # The 16384-token sweep: N 512..16k, B = 16384 / N; d 128 (H16), d 64
+        # (H32) and d 96 zero-padded to 128 (H16, credited with d = 96 work);
+        # both masks; seeded N(0,1) inputs.
+        print(f"[bench] 16384-token sweep: {a.sweep_reps} launches per configuration",
+              file=sys.stderr, flush=True)
+        rows = []
+        for wnc in workloads.sweep(False):
+            x = [dev_bf16(t) for t in workloads.gen_qkv(wnc)]
+            ox = torch.empty_like(x[0])
+            lx = torch.empty((wnc.B, wnc.H, wnc.N), dtype=torch.float32, device=dev)
+            for causal in (False, True):
+                wc = workloads.Workload(wnc.name.replace("_nc", "_c") if causal else wnc.name,
+                                        wnc.B, wnc.H, wnc.N, wnc.d, causal, wnc.seed,
+                                        d_logical=wnc.d_logical)
+                t = time_reps(lambda: ea.attn_fwd_bf16(*x, causal=causal,
+                                                       softmax_scale=wc.softmax_scale, out=ox,
+                                                       lse=lx), a.sweep_reps, stream)
+                tf = wc.flops() / t / 1e12
+                rows.append({"workload": wc.name, "B": wc.B, "H": wc.H, "N": wc.N, "d": wc.d,
+                             "d_counted": wc.d_logical or wc.d, "causal": causal,
+                             "value": round(tf, 2),
+                             "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                             "ms": round(t * 1e3, 4),
+                             "finite": bool(torch.isfinite(ox).all().item())})
+            del x, ox, lx
+        out["sweep"] = {"kernel": "attn_fwd_bf16", "unit": "TFLOP/s",
+                        "flops_counted": "4 B H N^2 d (d = 96 for the padded runs), halved for "
+                                         "causal", "timing": "median of per-call HIP event times",
+                        "configs": rows}
+    if a.long_reps > 0:
+        # Long single request: B1 H8 N32768 d128 causal (seed 5), bf16, and the
+        # same inputs through the FP8 path (pre-pass untimed).
+        print(f"[bench] long request B1 H8 N32768 causal: {a.long_reps} launches",
+              file=sys.stderr, flush=True)
+        wl = workloads.LONG
+        xl = [dev_bf16(t) for t in workloads.gen_qkv(wl)]
+        ol = torch.empty_like(xl[0])
+        ll = torch.empty((wl.B, wl.H, wl.N), dtype=torch.float32, device=dev)
+        t = time_reps(lambda: ea.attn_fwd_bf16(*xl, causal=True, softmax_scale=wl.softmax_scale,
+                                               out=ol, lse=ll), a.long_reps, stream)
+        c8 = [ea.blockquant_hadamard(xl[0], signs, 128), ea.blockquant_hadamard(xl[1], signs, 128),
+              ea.blockquant_hadamard(xl[2], None, 128)]
+        t8l = time_reps(lambda: ea.attn_fwd_fp8(c8[0][0], c8[1][0], c8[2][0], c8[0][1], c8[1][1],
+                                                c8[2][1], causal=True,
+                                                softmax_scale=wl.softmax_scale, out=ol, lse=ll),
+                        a.long_reps, stream)
+        f = wl.flops()
+        out["long_c5"] = {
+            "workload": wl.name, "flops_counted": "2 B H N^2 d (visible pairs)",
+            "timing": "median of per-call HIP event times",
+            "attn_fwd_bf16": {"value": round(f / t / 1e12, 2),
+                              "pct_of_peak": round(100 * f / t / 1e12 / PEAK_BF16_TFLOPS, 2),
+                              "ms": round(t * 1e3, 4)},
+            "attn_fwd_fp8": {"value": round(f / t8l / 1e12, 2),
+                             "pct_of_peak": round(100 * f / t8l / 1e12 / PEAK_FP8_TFLOPS, 2),
+                             "ms": round(t8l * 1e3, 4)},
+            "finite": bool(torch.isfinite(ol).all().item())}
+        del xl, ol, ll, c8
+    if not a.no_fp8_accuracy and a.d == 128 and a.N == 8192 and a.B8 == 4 and a.H == 16:
+        # FP8 accuracy on both outlier distributions: the GPU path (pre-pass +
+        # forward) against an fp64 evaluation of exact attention on 512 sampled
+        # rows, for block vs per-tensor scales x rotation vs none; beside it the
+        # oracle's emulation floor of each case (stored by
+        # tests/golden/make_fp8_emulation_floor.py on the same rows).
+        print("[bench] fp8 accuracy and ablation", file=sys.stderr, flush=True)
+        floor_path = os.path.join(ROOT, "tests", "golden", "fp8_emulation_floor.json")
+        floors = json.load(open(floor_path)) if os.path.exists(floor_path) else {}
+        acc = {"reference": "fp64 exact attention of the bf16 inputs on the device, 4 heads x "
+                            "128 sampled rows", "workload": "B4 H16 N8192 d128 non-causal"}
+        for key, wa in (("fp8_outlier30", w8),
+                        ("fp8_page_outlier_sd10", workloads.Workload(
+                            "fp8_page", B8, H, N, d, False, seed=3, dist="outlier_sd10"))):
+            xa = [q8in, k8in, v8in] if wa is w8 else [dev_bf16(t) for t in workloads.gen_qkv(wa)]
+            sel = workloads.fp8_accuracy_rows(N)
+            ref = torch.cat([fp64_rows_reference(*xa, b, h, r, scale) for b, h, r in sel])
+            res = {"rms_exact": round(float(ref.pow(2).mean().sqrt()), 6)}
+            for br, rot in ((128, True), (128, False), (0, True), (0, False)):
+                sg = signs if rot else None
+                cq = [ea.blockquant_hadamard(xa[0], sg, br), ea.blockquant_hadamard(xa[1], sg, br),
+                      ea.blockquant_hadamard(xa[2], None, br)]
+                oa, _ = ea.attn_fwd_fp8(cq[0][0], cq[1][0], cq[2][0], cq[0][1], cq[1][1], cq[2][1],
+                                        softmax_scale=scale)
+                got = torch.cat([oa[b, torch.as_tensor(r, device=dev), h].double()
+                                 for b, h, r in sel])
+                name = f"{'block' if br else 'per_tensor'}_{'rotation' if rot else 'no_rotation'}"
+                res[name] = {"rmse": round(float((got - ref).pow(2).mean().sqrt()), 6),
+                             "emulation_floor": floors.get(key, {}).get(name)}
+            res["ratio_per_tensor_no_rotation_to_block_rotation"] = round(
+                res["per_tensor_no_rotation"]["rmse"] / res["block_rotation"]["rmse"], 3)
+            acc[key] = res
+            del xa
+        out["fp8_accuracy"] = acc
     if not a.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w16, a.cpu_seconds)

@@ -155,6 +155,17 @@ def sample_rows(B: int, H: int, N: int, count: int, seed: int) -> np.ndarray:
     return np.stack([b, h, i], axis=1).astype(np.int64)
 
 
+# (b, h) heads of the FP8 workload whose sampled query rows the FP8 accuracy
+# figures are taken on (128 rows each, seed 77 + h)
+FP8_ACCURACY_HEADS = ((0, 0), (1, 5), (2, 10), (3, 15))
+
+
+def fp8_accuracy_rows(N: int):
+    """[(b, h, rows)] for the FP8 accuracy figures: 128 sampled query rows in
+    each head of FP8_ACCURACY_HEADS (rows as int64 indices into the sequence)."""
+    return [(b, h, sample_rows(1, 1, N, 128, seed=77 + h)[:, 2]) for b, h in FP8_ACCURACY_HEADS]
+
+
 def to_bf16_f32(x: np.ndarray) -> np.ndarray:
     """Round float32 -> bfloat16 (RNE, via torch) and return the values as float32."""
     import torch
