@@ -146,6 +146,9 @@ __device__ __forceinline__ void copy_offsets(int wave, int lane, uint32_t row_by
 
 // ---------------------------------------------------------------------------
 // D_i = sum_c dO[i, c] O[i, c] and LSE_i * log2(e); D / 8 lanes per row.
+// Rows are taken in [B, H, N] order (the order of D and the LSE), so a
+// workgroup's D and LSE stores are contiguous and coalesced; each row's O and
+// dO reads are whole rows of the BSHD tensors (2 D bytes each).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* __restrict__ O,
                                                        const __bf16* __restrict__ dO,
@@ -154,10 +157,13 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* __restrict_
                                                        float* __restrict__ L2, int H, int N,
                                                        int64_t rows) {
   constexpr int LPR = D / 8;
-  const int64_t r = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  const int64_t idx = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;  // [B, H, N] index
   const int c = threadIdx.x % LPR;
   float acc = 0.f;
-  if (r < rows) {
+  if (idx < rows) {
+    const int64_t n = idx % N, bh = idx / N;
+    const int64_t h = bh % H, b = bh / H;
+    const int64_t r = (b * N + n) * H + h;  // BSHD row
     const bf16x8 o = *(const bf16x8*)(O + r * D + 8 * c);
     const bf16x8 g = *(const bf16x8*)(dO + r * D + 8 * c);
 #pragma unroll
@@ -165,11 +171,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* __restrict_
   }
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m, 64);
-  if (r < rows && c == 0) {
-    // BSHD row r = (b N + n) H + h  ->  [B, H, N] index (b H + h) N + n
-    const int64_t h = r % H, bn = r / H;
-    const int64_t n = bn % N, b = bn / N;
-    const int64_t idx = (b * H + h) * N + n;
+  if (idx < rows && c == 0) {
     Drow[idx] = acc;
     L2[idx] = LSE[idx] * kLog2e;
   }
