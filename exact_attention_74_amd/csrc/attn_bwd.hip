@@ -113,6 +113,101 @@ __device__ __forceinline__ void mfma_tr_counted(bf16x8 (&frag)[2][NE], const bf1
   });
 }
 
+// The same eight products for NE = 4 as one block of assembly on accumulators
+// held in AGPRs (dV^T and dK^T stay in the AGPR file for the whole kernel, so
+// the S and dP products and the softmax keep the 256 VGPRs).  Each MFMA waits
+// only for its own two reads (LDS reads complete in issue order); the leading
+// s_nop gives the two wait states an MFMA needs after a VALU write of its B
+// operand.  Back-to-back products on one accumulator need no wait states.
+__device__ __forceinline__ void mfma_tr_agpr4(bf16x8 (&f)[2][4], const bf16x8 (&b)[2],
+                                              f32x16 (&acc)[4]) {
+  asm volatile(
+      "s_waitcnt lgkmcnt(14)\n\t"
+      "s_nop 1\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %4, %12, %0\n\t"
+      "s_waitcnt lgkmcnt(12)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %5, %13, %0\n\t"
+      "s_waitcnt lgkmcnt(10)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %6, %12, %1\n\t"
+      "s_waitcnt lgkmcnt(8)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %7, %13, %1\n\t"
+      "s_waitcnt lgkmcnt(6)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %2, %8, %12, %2\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %2, %9, %13, %2\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %3, %10, %12, %3\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %3, %11, %13, %3"
+      : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3])
+      : "v"(f[0][0]), "v"(f[1][0]), "v"(f[0][1]), "v"(f[1][1]), "v"(f[0][2]), "v"(f[1][2]),
+        "v"(f[0][3]), "v"(f[1][3]), "v"(b[0]), "v"(b[1]));
+}
+
+// Wait states between the AGPR accumulators' last MFMA (or their zeroing
+// writes) and any other instruction that touches them.
+__device__ __forceinline__ void agpr_fence(f32x16 (&a)[4], f32x16 (&b)[4]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]), "+a"(b[0]), "+a"(b[1]),
+                 "+a"(b[2]), "+a"(b[3]));
+}
+
+// Read stream of the software-pipelined head-dim-128 tile body: per 32-query
+// block, 56 LDS reads in this order
+//   [0, 8)   Q row fragments (A operands of S = Q K^T, one per MFMA)
+//   [8, 12)  LSE * log2(e) of the block's rows
+//   [12, 20) dO row fragments (A operands of dP = dO V^T)
+//   [20, 24) D of the block's rows
+//   [24, 40) dO^T transposed halves (two per dV^T MFMA)
+//   [40, 56) Q^T transposed halves (two per dK^T MFMA)
+// and 32 MFMA slots: S (8), dP (8), dV^T (8), dK^T (8).  Slot s needs the
+// stream up to need(s); before its MFMA the reads up to issued(s), kLook past
+// that, have been issued, so the wait is lgkmcnt(issued(s) - need(s)) (LDS
+// reads complete in issue order).  The LSE and D reads precede the first dP
+// and dV reads, so the waits of those slots cover them too.
+namespace pipe128 {
+constexpr int kRPB = 56;
+constexpr int kLast = 2 * kRPB - 1;  // two blocks per 64-row tile
+constexpr int kLook = 8;
+constexpr int need(int s) {
+  return (s / 32) * kRPB + ((s % 32) < 8    ? (s % 32)
+                            : (s % 32) < 16 ? 12 + (s % 32 - 8)
+                            : (s % 32) < 24 ? 24 + 2 * (s % 32 - 16) + 1
+                                            : 40 + 2 * (s % 32 - 24) + 1);
+}
+constexpr int issued(int s) {
+  return s < 0 ? -1 : (need(s) + kLook < kLast ? need(s) + kLook : kLast);
+}
+static_assert(issued(63) == kLast, "every read is issued");
+}  // namespace pipe128
+
+template <int N>
+__device__ __forceinline__ void wait_lds_pair(bf16x4& a, bf16x4& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void wait_lds_rows(bf16x8& x, f32x4 (&r)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(%5)"
+               : "+v"(x), "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3])
+               : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void wait_lds_pair_rows(bf16x4& a, bf16x4& b, f32x4 (&r)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(%6)"
+               : "+v"(a), "+v"(b), "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3])
+               : "n"(N));
+}
+
+// acc += a x b on an AGPR accumulator (one dV^T or dK^T product); NOP2 puts
+// the two wait states an MFMA needs after a VALU write of its B operand.
+template <bool NOP2>
+__device__ __forceinline__ void mfma_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  if constexpr (NOP2)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
 // LDS address of this lane's transposed-read source in a tile at LDS byte
 // address `base` (rows key-major, chunk swizzle swz_b): row 4 hv + j, chunk
 // 4 e + 2 (g % 2) + q / 2, half q % 2.
@@ -315,10 +410,13 @@ __global__ __launch_bounds__(64 * kNWb, 2) void bwd_dq_kernel(
 // ---------------------------------------------------------------------------
 // dK, dV.  LDS: [2 stages x (LSE*log2e[64], D[64])] then 2 stages x (Q tile,
 // dO tile), both tiles swz_b (read row-wise and transposed).
-// Two waves per SIMD where the kernel fits 256 registers without spilling
-// (d = 64, causal: 246); elsewhere one, with up to 512.
+// Head dim 64: two waves per SIMD (at most 250 VGPRs, every MFMA in VGPR
+// form).  Head dim 128: one wave per SIMD; dV^T and dK^T (128 registers)
+// live in the AGPR file, accumulated by assembly MFMAs, so that K^T, V^T, the
+// fragments and the softmax keep the 256 VGPRs, and the unmasked tiles run
+// the software-pipelined body tile_pipe.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(64 * kNWb, (D == 64 && CAUSAL) ? 2 : 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(64 * kNWb, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Drow,
     __bf16* __restrict__ dK, __bf16* __restrict__ dV, int H, int Hkv, int N, float scale_log2,
@@ -396,6 +494,7 @@ __global__ __launch_bounds__(64 * kNWb, (D == 64 && CAUSAL) ? 2 : 1) void bwd_dk
   f32x16 dvacc[NE], dkacc[NE];
 #pragma unroll
   for (int e = 0; e < NE; ++e) dvacc[e] = dkacc[e] = f32x16{};
+  if constexpr (NE == 4) agpr_fence(dvacc, dkacc);
 
   auto tile = [&](auto st, auto masked, int i0) __attribute__((always_inline)) {
     constexpr int ST = decltype(st)::value;
@@ -403,7 +502,7 @@ __global__ __launch_bounds__(64 * kNWb, (D == 64 && CAUSAL) ? 2 : 1) void bwd_dk
     static_for<2>([&](auto JQ) __attribute__((always_inline)) {
       constexpr int jq = decltype(JQ)::value;
       const int iq0 = i0 + 32 * jq;
-      if (CAUSAL && iq0 + 31 < k0w) return;  // every query before every key of this wave
+      if (MASKED && CAUSAL && iq0 + 31 < k0w) return;  // every query before every key of this wave
       bf16x8 f[NF];
       static_for<NF>([&](auto T) __attribute__((always_inline)) {
         constexpr int t = decltype(T)::value;
@@ -436,28 +535,153 @@ __global__ __launch_bounds__(64 * kNWb, (D == 64 && CAUSAL) ? 2 : 1) void bwd_dk
       }
       bf16x8 tf[2][NE];
       read_tr_frags<D, ST * G::STAGE + G::TILE, jq>(taddr, tf);  // dO^T
-      mfma_tr_counted<NE>(tf, pb, dvacc);
+      if constexpr (NE == 4) mfma_tr_agpr4(tf, pb, dvacc);
+      else mfma_tr_counted<NE>(tf, pb, dvacc);
       read_tr_frags<D, ST * G::STAGE, jq>(taddr, tf);  // Q^T
-      mfma_tr_counted<NE>(tf, dsb, dkacc);
+      if constexpr (NE == 4) mfma_tr_agpr4(tf, dsb, dkacc);
+      else mfma_tr_counted<NE>(tf, dsb, dkacc);
+    });
+  };
+
+  // Head dim 128, unmasked tiles: the tile's two 32-query blocks as one
+  // software pipeline of 64 MFMA slots (see pipe128).  P of a block is
+  // computed two rows at a time under its dP products and dS under its dV^T
+  // products, about five VALU instructions per MFMA; each slot ends in a
+  // scheduling barrier so that this interleave is kept, and each slot's VALU
+  // results are pinned in place by an empty assembly use.  The arithmetic and
+  // its order are those of the tile body above.
+  auto tile_pipe = [&](auto st, int i0) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st)::value;
+    (void)i0;
+    bf16x8 fq[2][8], fg[2][8];
+    f32x4 l4[2][4], d4[2][4];
+    bf16x4 tlo[2][8], thi[2][8], qlo[2][8], qhi[2][8];
+    f32x16 sacc[2], dpacc[2];
+    float pr[2][16], fa[2][16], dd[2][16], dsv[2][16];
+    uint32_t pw[2][8], dw[2][8];
+    auto issue = [&](auto P_) __attribute__((always_inline)) {
+      constexpr int P = decltype(P_)::value;
+      constexpr int b = P / pipe128::kRPB, q = P % pipe128::kRPB;
+      if constexpr (q < 8) {
+        fq[b][q] = read_b128<ST * G::STAGE + b * 32 * G::RB>(qa0 ^ (uint32_t)(32 * q));
+      } else if constexpr (q < 12) {
+        l4[b][q - 8] = read_f4<ST * 512 + (32 * b + 8 * (q - 8)) * 4>(la0);
+      } else if constexpr (q < 20) {
+        fg[b][q - 12] =
+            read_b128<ST * G::STAGE + G::TILE + b * 32 * G::RB>(qa0 ^ (uint32_t)(32 * (q - 12)));
+      } else if constexpr (q < 24) {
+        d4[b][q - 20] = read_f4<ST * 512 + 256 + (32 * b + 8 * (q - 20)) * 4>(la0);
+      } else {
+        constexpr bool isq = q >= 40;
+        constexpr int r = isq ? q - 40 : q - 24;
+        constexpr int k = r / 2, half = r % 2, e = k / 2, T = k % 2;
+        constexpr int OFF = ST * G::STAGE + (isq ? 0 : G::TILE) + (32 * b + 16 * T + 8 * half) * G::RB;
+        const bf16x4 v = read_tr16<OFF>(half ? (taddr[e] ^ 32u) : taddr[e]);
+        if constexpr (isq) {
+          if constexpr (half) qhi[b][k] = v; else qlo[b][k] = v;
+        } else {
+          if constexpr (half) thi[b][k] = v; else tlo[b][k] = v;
+        }
+      }
+    };
+    auto join = [](const bf16x4& lo, const bf16x4& hi) __attribute__((always_inline)) {
+      return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    auto words = [](const uint32_t* w) __attribute__((always_inline)) {
+      return __builtin_bit_cast(bf16x8, i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]});
+    };
+    static_for<64>([&](auto S_) __attribute__((always_inline)) {
+      constexpr int s = decltype(S_)::value;
+      constexpr int b = s / 32, j = s % 32, ph = j / 8, i = j % 8;
+      constexpr int first = pipe128::issued(s - 1) + 1;
+      static_for<pipe128::issued(s) - pipe128::issued(s - 1)>([&](auto K_) __attribute__((always_inline)) {
+        issue(IC<first + decltype(K_)::value>{});
+      });
+      constexpr int W = pipe128::issued(s) - pipe128::need(s);
+      if constexpr (ph == 0) {  // S = Q K^T
+        wait_lds<W>(fq[b][i]);
+        sacc[b] = mfma_bf16(fq[b][i], kt[i], i == 0 ? f32x16{} : sacc[b]);
+      } else if constexpr (ph == 1) {  // dP = dO V^T; P two rows per slot
+        if constexpr (i == 0) wait_lds_rows<W>(fg[b][0], l4[b]);
+        else wait_lds<W>(fg[b][i]);
+        dpacc[b] = mfma_bf16(fg[b][i], vt[i], i == 0 ? f32x16{} : dpacc[b]);
+        __builtin_amdgcn_sched_barrier(0);  // the MFMA issues before the VALU that waits on S
+        // exp2 arguments of the next slot's rows, exponentials of this slot's,
+        // bf16 pair of the previous slot's: no instruction waits on a result
+        // of its own slot.
+        static_for<2>([&](auto U_) __attribute__((always_inline)) {
+          constexpr int u = decltype(U_)::value;
+          if constexpr (i == 0)
+            fa[b][u] = __builtin_fmaf(sacc[b][u], scale_log2, -l4[b][0][u]);
+          if constexpr (i < 7) {
+            constexpr int v = 2 * i + 2 + u;
+            fa[b][v] = __builtin_fmaf(sacc[b][v], scale_log2, -l4[b][v >> 2][v & 3]);
+          }
+          pr[b][2 * i + u] = exp2_fast(fa[b][2 * i + u]);
+        });
+        if constexpr (i >= 1) pw[b][i - 1] = pack_bf16x2(pr[b][2 * i - 2], pr[b][2 * i - 1]);
+        asm volatile("" : "+v"(pr[b][2 * i]), "+v"(pr[b][2 * i + 1]));
+        if constexpr (i < 7) asm volatile("" : "+v"(fa[b][2 * i + 2]), "+v"(fa[b][2 * i + 3]));
+        if constexpr (i >= 1) asm volatile("" : "+v"(pw[b][i - 1]));
+      } else if constexpr (ph == 2) {  // dV^T += dO^T P; dS two rows per slot
+        if constexpr (i == 0) wait_lds_pair_rows<W>(tlo[b][i], thi[b][i], d4[b]);
+        else wait_lds_pair<W>(tlo[b][i], thi[b][i]);
+        mfma_agpr<i <= 1>(dvacc[i / 2], join(tlo[b][i], thi[b][i]), words(&pw[b][4 * (i % 2)]));
+        __builtin_amdgcn_sched_barrier(0);  // the MFMA issues before the VALU that waits on dP
+        if constexpr (i == 0) {
+          pw[b][7] = pack_bf16x2(pr[b][14], pr[b][15]);
+          asm volatile("" : "+v"(pw[b][7]));
+        }
+        static_for<2>([&](auto U_) __attribute__((always_inline)) {
+          constexpr int u = decltype(U_)::value;
+          if constexpr (i == 0) dd[b][u] = dpacc[b][u] - d4[b][0][u];
+          if constexpr (i < 7) {
+            constexpr int v = 2 * i + 2 + u;
+            dd[b][v] = dpacc[b][v] - d4[b][v >> 2][v & 3];
+          }
+          dsv[b][2 * i + u] = pr[b][2 * i + u] * dd[b][2 * i + u];
+        });
+        if constexpr (i >= 1) dw[b][i - 1] = pack_bf16x2(dsv[b][2 * i - 2], dsv[b][2 * i - 1]);
+        asm volatile("" : "+v"(dsv[b][2 * i]), "+v"(dsv[b][2 * i + 1]));
+        if constexpr (i < 7) asm volatile("" : "+v"(dd[b][2 * i + 2]), "+v"(dd[b][2 * i + 3]));
+        if constexpr (i >= 1) asm volatile("" : "+v"(dw[b][i - 1]));
+      } else {  // dK^T += Q^T dS
+        wait_lds_pair<W>(qlo[b][i], qhi[b][i]);
+        mfma_agpr<i <= 1>(dkacc[i / 2], join(qlo[b][i], qhi[b][i]), words(&dw[b][4 * (i % 2)]));
+        if constexpr (i == 0) {
+          __builtin_amdgcn_sched_barrier(0);
+          dw[b][7] = pack_bf16x2(dsv[b][14], dsv[b][15]);
+          asm volatile("" : "+v"(dw[b][7]));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     });
   };
 
   // Query tiles: causal starts at the tile holding the workgroup's first key.
+  // The tiles run in three loops of whole pairs (stage 0, stage 1) so that the
+  // hot middle loop holds one copy of the unmasked tile body and no branch
+  // that the accumulators' registers would have to be reconciled across:
+  //   head   [qt0, qt_lo)   causal only: the two tiles that hold the
+  //                         workgroup's keys (masked; waves skip what lies
+  //                         entirely before their keys)
+  //   middle [qt_lo, qt_hi) unmasked: no query past N, none before a key
+  //   tail   [qt_hi, nqt)   masked: the rest, including a ragged last tile
   const int nqt = ceil_div(N, kBC);
   const int qt0 = CAUSAL ? (kblk * kRowsB) / kBC : 0;
-#define STEP(ST_, QT)                                                                            \
+  static_assert(kRowsB == 2 * kBC, "the causal head is one pair of tiles");
+  const int qt_lo = CAUSAL ? min(nqt, qt0 + 2) : qt0;
+  const int n_full = N / kBC;
+  const int qt_hi = n_full > qt_lo ? qt_lo + ((n_full - qt_lo) & ~1) : qt_lo;
+#define STEP(ST_, QT, MASKED_)                                                                   \
   do {                                                                                          \
     const int qt_ = (QT);                                                                       \
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                           \
     __syncthreads(); /* tile qt_ resident; every wave is done with the other stage */           \
     if (qt_ + 1 < nqt) load_tile((ST_) ^ 1, (qt_ + 1) * kBC);                                   \
     const int i0_ = qt_ * kBC;                                                                  \
-    if (!(CAUSAL && i0_ + kBC - 1 < k0w)) {                                                     \
-      if (i0_ + kBC > N || (CAUSAL && i0_ < k0w + 31))                                          \
-        tile(IC<ST_>{}, IC<1>{}, i0_);                                                          \
-      else                                                                                      \
-        tile(IC<ST_>{}, IC<0>{}, i0_);                                                          \
-    }                                                                                           \
+    if constexpr (NE == 4 && !(MASKED_)) tile_pipe(IC<ST_>{}, i0_);                              \
+    else if (!(MASKED_) || !(CAUSAL && i0_ + kBC - 1 < k0w)) tile(IC<ST_>{}, IC<MASKED_>{}, i0_); \
   } while (0)
   for (int g = 0; g < grp; ++g) {
     set_head(hk * grp + g);
@@ -465,16 +689,24 @@ __global__ __launch_bounds__(64 * kNWb, (D == 64 && CAUSAL) ? 2 : 1) void bwd_dk
     if (g > 0) __syncthreads();
     load_tile(0, qt0 * kBC);
     int qt = qt0;
-    for (; qt + 1 < nqt; qt += 2) {
-      STEP(0, qt);
-      STEP(1, qt + 1);
+    for (; qt < qt_lo; qt += 2) {
+      STEP(0, qt, 1);
+      if (qt + 1 < nqt) STEP(1, qt + 1, 1);
     }
-    if (qt < nqt) STEP(0, qt);
+    for (; qt < qt_hi; qt += 2) {
+      STEP(0, qt, 0);
+      STEP(1, qt + 1, 0);
+    }
+    for (; qt < nqt; qt += 2) {
+      STEP(0, qt, 1);
+      if (qt + 1 < nqt) STEP(1, qt + 1, 1);
+    }
   }
 #undef STEP
   // dK and dV rows stored whole through LDS (every wave is done with the
   // tiles after the barrier; each wave takes 2 * 32 * 2D bytes of them).
   static_assert(kNWb * 2 * 32 * 2 * D <= 2 * G::STAGE, "the dK/dV rows are staged in the tile buffers");
+  if constexpr (NE == 4) agpr_fence(dvacc, dkacc);
   __syncthreads();
   char* ob = tiles + wave * 2 * 32 * (2 * D);
   store_rows_via_lds<D>(ob, dkacc, scale, dK, kv_off, rs_kv, k0w, N, lane);
