@@ -161,10 +161,16 @@ __device__ __forceinline__ void agpr_fence(f32x16 (&a)[4], f32x16 (&b)[4]) {
 //   [24, 40) dO^T transposed halves (two per dV^T MFMA)
 //   [40, 56) Q^T transposed halves (two per dK^T MFMA)
 // and 32 MFMA slots: S (8), dP (8), dV^T (8), dK^T (8).  Slot s needs the
-// stream up to need(s); before its MFMA the reads up to issued(s), kLook past
-// that, have been issued, so the wait is lgkmcnt(issued(s) - need(s)) (LDS
-// reads complete in issue order).  The LSE and D reads precede the first dP
-// and dV reads, so the waits of those slots cover them too.
+// stream up to need(s).  A prologue issues reads 0 .. kLook; slot s issues,
+// right after its MFMA, the reads up to issued(s) = need(s) + kLook, so at
+// slot s's wait the reads up to issued(s - 1) are in flight and the wait is
+// lgkmcnt(issued(s - 1) - need(s)) (LDS reads complete in issue order).  The
+// LSE and D reads precede the first dP and dV reads, so the waits of those
+// slots cover them too.  Each slot runs: wait, MFMA, the reads ahead, then
+// its VALU work: an MFMA's first cycles after issue take LDS and scalar
+// instructions better than VALU ones (measured: 16 slots of MFMA + 5 VALU +
+// one read took 932 cycles with the VALU right after the MFMA, 812 with the
+// read first).
 namespace pipe128 {
 constexpr int kRPB = 56;
 constexpr int kLast = 2 * kRPB - 1;  // two blocks per 64-row tile
@@ -176,7 +182,7 @@ constexpr int need(int s) {
                                             : 40 + 2 * (s % 32 - 24) + 1);
 }
 constexpr int issued(int s) {
-  return s < 0 ? -1 : (need(s) + kLook < kLast ? need(s) + kLook : kLast);
+  return s < 0 ? kLook : (need(s) + kLook < kLast ? need(s) + kLook : kLast);
 }
 static_assert(issued(63) == kLast, "every read is issued");
 }  // namespace pipe128
@@ -593,19 +599,32 @@ __global__ __launch_bounds__(64 * kNWb, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     static_for<64>([&](auto S_) __attribute__((always_inline)) {
       constexpr int s = decltype(S_)::value;
       constexpr int b = s / 32, j = s % 32, ph = j / 8, i = j % 8;
-      constexpr int first = pipe128::issued(s - 1) + 1;
-      static_for<pipe128::issued(s) - pipe128::issued(s - 1)>([&](auto K_) __attribute__((always_inline)) {
-        issue(IC<first + decltype(K_)::value>{});
-      });
-      constexpr int W = pipe128::issued(s) - pipe128::need(s);
+      // reads for later slots are issued right after this slot's MFMA (they
+      // fill its operand-fetch cycles, which VALU instructions cannot use)
+      constexpr int first = pipe128::issued(s - 1) + 1;  // (slot 0: after the prologue's)
+      auto issue_ahead = [&]() __attribute__((always_inline)) {
+        static_for<pipe128::issued(s) - pipe128::issued(s - 1)>([&](auto K_) __attribute__((always_inline)) {
+          issue(IC<first + decltype(K_)::value>{});
+        });
+      };
+      if constexpr (s == 0) {  // prologue: the first kLook + 1 reads
+        static_for<pipe128::kLook + 1>([&](auto K_) __attribute__((always_inline)) {
+          issue(IC<decltype(K_)::value>{});
+        });
+      }
+      constexpr int W = pipe128::issued(s - 1) - pipe128::need(s);
+      static_assert(W >= 0, "this slot's reads were issued by earlier slots");
       if constexpr (ph == 0) {  // S = Q K^T
         wait_lds<W>(fq[b][i]);
         sacc[b] = mfma_bf16(fq[b][i], kt[i], i == 0 ? f32x16{} : sacc[b]);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_ahead();
       } else if constexpr (ph == 1) {  // dP = dO V^T; P two rows per slot
         if constexpr (i == 0) wait_lds_rows<W>(fg[b][0], l4[b]);
         else wait_lds<W>(fg[b][i]);
         dpacc[b] = mfma_bf16(fg[b][i], vt[i], i == 0 ? f32x16{} : dpacc[b]);
         __builtin_amdgcn_sched_barrier(0);  // the MFMA issues before the VALU that waits on S
+        issue_ahead();
         // exp2 arguments of the next slot's rows, exponentials of this slot's,
         // bf16 pair of the previous slot's: no instruction waits on a result
         // of its own slot.
@@ -628,6 +647,7 @@ __global__ __launch_bounds__(64 * kNWb, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         else wait_lds_pair<W>(tlo[b][i], thi[b][i]);
         mfma_agpr<i <= 1>(dvacc[i / 2], join(tlo[b][i], thi[b][i]), words(&pw[b][4 * (i % 2)]));
         __builtin_amdgcn_sched_barrier(0);  // the MFMA issues before the VALU that waits on dP
+        issue_ahead();
         if constexpr (i == 0) {
           pw[b][7] = pack_bf16x2(pr[b][14], pr[b][15]);
           asm volatile("" : "+v"(pw[b][7]));
@@ -648,6 +668,8 @@ __global__ __launch_bounds__(64 * kNWb, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
       } else {  // dK^T += Q^T dS
         wait_lds_pair<W>(qlo[b][i], qhi[b][i]);
         mfma_agpr<i <= 1>(dkacc[i / 2], join(qlo[b][i], qhi[b][i]), words(&dw[b][4 * (i % 2)]));
+        __builtin_amdgcn_sched_barrier(0);
+        issue_ahead();
         if constexpr (i == 0) {
           __builtin_amdgcn_sched_barrier(0);
           dw[b][7] = pack_bf16x2(dsv[b][14], dsv[b][15]);
