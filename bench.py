@@ -24,6 +24,7 @@ JSON line.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -376,15 +377,48 @@ def main():
             ea.attn_bwd_bf16(q, k, v, o16, lse16, do, causal=a.causal, softmax_scale=scale,
                              dq=dq, dk=dk, dv=dv, workspace=ws)
         t_bwd = time_reps(bwd, a.bwd_reps, stream)
+        bname = w16.name.replace("attn_fwd", "attn_bwd")
         bflops = 2.5 * w16.flops()  # five N^2 d products against the forward's two
         out["backward"] = {
-            "kernel": "attn_bwd_bf16 (prep + dK/dV + dQ kernels)", "workload": w16.name,
+            "kernel": "attn_bwd_bf16 (prep + dK/dV + dQ kernels)", "workload": bname,
             "value": round(bflops / t_bwd / 1e12, 2), "unit": "TFLOP/s",
             "flops_counted": "2.5 x forward (10 B H N^2 d, halved for causal)",
             "pct_of_peak": round(100 * bflops / t_bwd / 1e12 / PEAK_BF16_TFLOPS, 2),
             "ms": round(t_bwd * 1e3, 4), "reps": a.bwd_reps,
             "timing": "median of per-call HIP event times",
             "finite": bool(all(torch.isfinite(x).all().item() for x in (dq, dk, dv)))}
+        # The other mask on the same inputs, and head dim 64 (H doubled, the
+        # 16384-token sweep's d = 64 shape): the kernels' other instances.
+        variants = {}
+        print("[bench] backward variants: other mask, d = 64", file=sys.stderr, flush=True)
+        o_c, lse_c = ea.attn_fwd_bf16(q, k, v, causal=not a.causal, softmax_scale=scale)
+
+        def bwd_c():
+            ea.attn_bwd_bf16(q, k, v, o_c, lse_c, do, causal=not a.causal, softmax_scale=scale,
+                             dq=dq, dk=dk, dv=dv, workspace=ws)
+        t_c = time_reps(bwd_c, a.bwd_reps, stream)
+        fl_c = 2.5 * dataclasses.replace(w16, causal=not a.causal).flops()
+        variants["causal" if not a.causal else "non_causal"] = {
+            "workload": bname + ("_causal" if not a.causal else "_noncausal"),
+            "value": round(fl_c / t_c / 1e12, 2), "ms": round(t_c * 1e3, 4)}
+        del o_c, lse_c
+        if d == 128:
+            w64 = workloads.Workload(f"attn_bwd_b{B}h{2 * H}n{N}d64{sfx}", B, 2 * H, N, 64, a.causal,
+                                     seed=2)
+            q6, k6, v6 = (dev_bf16(x) for x in workloads.gen_qkv(w64))
+            do6 = dev_bf16(workloads.gen_random((B, N, 2 * H, 64), 1003))
+            o6, lse6 = ea.attn_fwd_bf16(q6, k6, v6, causal=a.causal, softmax_scale=w64.softmax_scale)
+            g6 = [torch.empty_like(q6) for _ in range(3)]
+
+            def bwd_64():
+                ea.attn_bwd_bf16(q6, k6, v6, o6, lse6, do6, causal=a.causal,
+                                 softmax_scale=w64.softmax_scale, dq=g6[0], dk=g6[1], dv=g6[2])
+            t_64 = time_reps(bwd_64, a.bwd_reps, stream)
+            variants["d64"] = {"workload": w64.name, "value": round(2.5 * w64.flops() / t_64 / 1e12, 2),
+                               "ms": round(t_64 * 1e3, 4),
+                               "finite": bool(all(torch.isfinite(x).all().item() for x in g6))}
+            del q6, k6, v6, do6, o6, lse6, g6
+        out["backward"]["variants"] = variants
     if a.rope_reps > 0:
         # The pre-pass fused with a rotary embedding (half-split pairs), on the
         # fp8 workload's Q; algorithmic bytes add the cos/sin tables, read once.
