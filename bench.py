@@ -64,6 +64,9 @@ def parse():
                         "skips them")
     p.add_argument("--causal-reps", type=int, default=20,
                    help="launches of the causal forwards on the same workloads (0: skip)")
+    p.add_argument("--pipe-reps", type=int, default=20,
+                   help="launches of the pipelined bf16 schedule and the same-phase kernel, "
+                        "alternated, at the bf16 workload and B4 H16 N4096 (0: skip)")
     p.add_argument("--d256-reps", type=int, default=20,
                    help="launches of the head-dim-256 forwards, B2 H8 N8192 (0: skip)")
     p.add_argument("--c2-reps", type=int, default=20,
@@ -456,6 +459,36 @@ def main():
                              "pct_of_peak": round(100 * f8 / t_c8 / 1e12 / PEAK_FP8_TFLOPS, 2),
                              "ms": round(t_c8 * 1e3, 4)},
             "finite": bool(torch.isfinite(o16).all().item() and torch.isfinite(o8).all().item())}
+    if a.pipe_reps > 0 and not a.causal and a.d == 128:
+        # The intra-wave pipelined schedule (attn_fwd_bf16_pipelined) against
+        # the same-phase kernel on the same inputs, alternated twice; the two
+        # must agree bit for bit.
+        print(f"[bench] pipelined schedule: {a.pipe_reps} launches x 2 rounds", file=sys.stderr,
+              flush=True)
+        legs = {}
+        for name, (Bp, Np) in (("headline", (B, N)), ("b4n4096", (4, 4096))):
+            if (Bp, Np) == (B, N):
+                qp, kp, vp, wp = q, k, v, w16
+            else:
+                wp = workloads.Workload(f"attn_fwd_b{Bp}h{H}n{Np}d{d}", Bp, H, Np, d, False, seed=2)
+                qp, kp, vp = (dev_bf16(x) for x in workloads.gen_qkv(wp))
+            op, lp = torch.empty_like(qp), torch.empty((Bp, H, Np), dtype=torch.float32, device=dev)
+            op2, lp2 = torch.empty_like(op), torch.empty_like(lp)
+            plain = lambda: ea.attn_fwd_bf16(qp, kp, vp, softmax_scale=scale, out=op, lse=lp)
+            piped = lambda: ea.attn_fwd_bf16_pipelined(qp, kp, vp, softmax_scale=scale, out=op2,
+                                                       lse=lp2)
+            tp, tq = [], []
+            for _ in range(2):
+                tp.append(time_reps(plain, a.pipe_reps, stream))
+                tq.append(time_reps(piped, a.pipe_reps, stream))
+            f = wp.flops()
+            legs[name] = {"workload": wp.name,
+                          "same_phase": round(f / min(tp) / 1e12, 2),
+                          "pipelined": round(f / min(tq) / 1e12, 2),
+                          "bit_identical": bool(torch.equal(op, op2) and torch.equal(lp, lp2))}
+        out["pipelined"] = {"kernel": "attn_fwd_bf16_pipelined", "unit": "TFLOP/s",
+                            "timing": "best of two medians of per-call HIP event times, alternated",
+                            **legs}
     if a.d256_reps > 0:
         # Head dim 256 (the report's best FP8 case), B2 H8 N8192: the 2048-wide
         # model at d = 256.  FP8 codes from the pre-pass (untimed here).

@@ -67,7 +67,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? EXATTN_OK : EXATTN_ERR_H
 
 extern "C" {
 
-int exattn_abi_version(void) { return 7; }
+int exattn_abi_version(void) { return 8; }
 
 const char* exattn_strerror(int code) {
   switch (code) {
@@ -88,9 +88,10 @@ const char* exattn_strerror(int code) {
   }
 }
 
-int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                      int H, int H_kv, int N, int d, int causal, float softmax_scale,
-                      void* stream) {
+namespace {
+int fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+             int H_kv, int N, int d, int causal, float softmax_scale, void* stream,
+             bool pipelined) {
   int rc = check_shape(B, H, N, d, 2);
   if (rc) return rc;
   if (!good_heads(H, H_kv)) return EXATTN_ERR_SHAPE;
@@ -105,12 +106,25 @@ int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, void* o, floa
   if (aliased({{o, bytes}, {lse, (int64_t)B * H * N * 4}}, {{q, bytes}, {k, kv_bytes}, {v, kv_bytes}}))
     return EXATTN_ERR_VALUE;
   return hip_status(exattn::launch_attn_fwd_bf16(q, k, v, o, lse, B, H, H_kv, N, d, causal != 0,
-                                                 softmax_scale, (hipStream_t)stream));
+                                                 softmax_scale, (hipStream_t)stream, pipelined));
+}
+}  // namespace
+
+int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                      int H, int H_kv, int N, int d, int causal, float softmax_scale,
+                      void* stream) {
+  return fwd_bf16(q, k, v, o, lse, B, H, H_kv, N, d, causal, softmax_scale, stream, false);
 }
 
 int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                   int N, int d, int causal, float softmax_scale, void* stream) {
-  return attn_fwd_bf16_gqa(q, k, v, o, lse, B, H, H, N, d, causal, softmax_scale, stream);
+  return fwd_bf16(q, k, v, o, lse, B, H, H, N, d, causal, softmax_scale, stream, false);
+}
+
+int attn_fwd_bf16_pipelined(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int N, int d, int causal, float softmax_scale,
+                            void* stream) {
+  return fwd_bf16(q, k, v, o, lse, B, H, H, N, d, causal, softmax_scale, stream, true);
 }
 
 int attn_fwd_fp8_gqa(const void* q8, const void* k8, const void* v8, const float* q_scale,

@@ -171,6 +171,35 @@ __device__ __forceinline__ void tile_compute(const char* smem, const uint32_t (&
 #undef TR_PAIR
 }
 
+// Software-pipelined interior tiles (the pipelined entry point, head dim 128,
+// non-causal, 8-wave workgroups).  The FlashAttention-3 report (section 3.2)
+// issues the next block's S = Q K^T before the current block's softmax so
+// that the matrix cores work while the exponentials run.  Here iteration j of
+// a wave issues 32 MFMAs as 32 slots: the 16 of S(j+1) = K(j+1) Q^T, then the
+// 16 of O^T += V(j)^T P(j)^T.  Between them run the VALU work of tile j's
+// softmax and S(j+1)'s row max (slots 24-31): exponential v (with its
+// multiply-add and row-sum add) in slot 7v / 8 of slots 0-27, about one per
+// MFMA, and each bf16 pair packed in the slot of its second exponential, so
+// every P^T operand is complete before its first MFMA (measured 0.8% faster
+// than two exponentials in each of 16 slots).  Each MFMA's K or V^T fragment is read
+// kLook reads ahead and waited for with an exact lgkmcnt count.  K is loaded
+// one tile ahead of V in the same two LDS stages (no extra LDS).  Every output
+// element goes through the same operations in the same order as in the
+// same-phase loop, so the results are bit-identical to it.
+namespace fpipe {
+constexpr int kLook = 8;   // LDS reads in flight ahead of the MFMA that needs them
+constexpr int kLast = 47;  // reads per iteration - 1: 16 K fragments + 32 V^T halves
+// Read index that slot s's MFMA needs last: K fragment s, or the second V^T
+// half of fragment s - 16.
+constexpr int need(int s) { return s < 16 ? s : 16 + 2 * (s - 16) + 1; }
+// Reads issued by the end of slot s (s = -1: the prologue).
+constexpr int issued(int s) {
+  return s < 0 ? kLook : (need(s) + kLook < kLast ? need(s) + kLook : kLast);
+}
+// Exponential v (0 .. 31) of tile j's P^T runs in slot exp_slot(v).
+constexpr int exp_slot(int v) { return (7 * v) / 8; }
+}  // namespace fpipe
+
 // One workgroup's work item: query block qblk (32 * NW rows) of head bh,
 // against every visible key.
 // Causal work runs persistent (d <= 128; at d = 256 the loop around the
@@ -178,7 +207,7 @@ __device__ __forceinline__ void tile_compute(const char* smem, const uint32_t (&
 template <int D, bool CAUSAL>
 constexpr bool persistent() { return CAUSAL && D <= 128; }
 
-template <int D, bool CAUSAL, int NW>
+template <int D, bool CAUSAL, int NW, bool PIPE>
 __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restrict__ Q,
                                              const __bf16* __restrict__ K,
                                              const __bf16* __restrict__ V, __bf16* __restrict__ O,
@@ -283,8 +312,197 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
       tile_compute<D, CAUSAL, MASKED, ST_>(smem, kaddr, vaddr, qf, oacc, m, l, kb_ * kBC, N, qi, \
                                            hh, scale_log2);                                     \
   } while (0)
-  LOAD_TILE(0, 0);
   int kb = 0;
+  if constexpr (PIPE && D == 128 && !CAUSAL && NW == 8) {
+    // The pipelined loop over the interior tiles 0 .. nkb_int - 1 (an even
+    // count, at least two; the edge tiles follow in the loops below).  LDS:
+    // K(j) sits in K slot j % 2 and V(j) in V slot j % 2 of the two stages,
+    // but K is loaded one tile ahead: iteration j reads K(j+1) and V(j) and
+    // starts the copies of K(j+2) and V(j+1) into the slots that K(j) and
+    // V(j-1) left free.  Its barrier certifies that K(j+1) and V(j) have
+    // landed and that every wave is done with those two slots.
+    if (nkb_int >= 2) {
+      const int nint = nkb_int;
+      auto load_k = [&](int slot, int k0) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t r = tile_rsrc(kh, (uint32_t)k0 * row_bytes, nbytes);
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i)
+          copy_to_lds16(r, smem + (wave * LOADS + i) * 1024 + G::koff(slot), voff_k[i]);
+      };
+      auto load_v = [&](int slot, int k0) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t r = tile_rsrc(vh, (uint32_t)k0 * row_bytes, nbytes);
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i)
+          copy_to_lds16(r, smem + (wave * LOADS + i) * 1024 + G::VBASE + G::voff(slot), voff_v[i]);
+      };
+      load_k(0, 0);
+      load_v(0, 0);
+      load_k(1, kBC);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      // S(0) ahead of the loop, as in the same-phase tile body.
+      f32x16 sA[2], sB[2];
+      {
+        constexpr int NK = 16, AHEAD = 8;
+        bf16x8 kf[NK];
+        auto rd = [&](auto I) __attribute__((always_inline)) {
+          constexpr int i = decltype(I)::value, t = i / 2, j = i % 2;
+          kf[i] = read_b128<G::koff(0) + j * 32 * G::RB>(kaddr[t]);
+        };
+        static_for<AHEAD>(rd);
+        static_for<NK>([&](auto I) __attribute__((always_inline)) {
+          constexpr int i = decltype(I)::value, t = i / 2, j = i % 2;
+          constexpr int issued = (AHEAD + i < NK) ? AHEAD + i : NK;
+          wait_lds<issued - i - 1>(kf[i]);
+          sA[j] = mfma_bf16(kf[i], qf[t], t == 0 ? f32x16{} : sA[j]);
+          if constexpr (i + AHEAD < NK) rd(IC<i + AHEAD>{});
+        });
+      }
+      float mx = max_halves(rowmax(sA));
+      // The lazy offset of the same-phase body: raised past 8 binades, with
+      // the rescale of l and O (after the previous tile's P.V MFMAs).
+      auto raise_offset = [&](float mxc) __attribute__((always_inline)) {
+        const float mb = mxc * scale_log2;
+        const bool raise = mb > m + kLazy;
+        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+          const float m_new = raise ? mb : m;
+          const float alpha = exp2_fast(m - m_new);
+          m = m_new;
+          l *= alpha;
+#pragma unroll
+          for (int e = 0; e < D / 32; ++e) oacc[e] *= alpha;
+        }
+      };
+      // Iteration j: K slot SK holds K(j+1), V slot SV holds V(j); cur = S(j),
+      // nxt receives S(j+1).
+      auto iter = [&](auto SK_, auto SV_, f32x16 (&cur)[2], f32x16 (&nxt)[2], int j)
+                      __attribute__((always_inline)) {
+        constexpr int SK = decltype(SK_)::value, SV = decltype(SV_)::value;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (j + 2 < nint) load_k(SV, (j + 2) * kBC);
+        if (j + 1 < nint) load_v(SK, (j + 1) * kBC);
+        raise_offset(mx);
+        const float neg_m = -m;
+        float rsum = 0.f;
+        uint32_t pw[16];  // P(j)^T as bf16 pairs
+        float pe[32];     // its exponentials
+        bf16x8 kf[16];
+        bf16x4 vlo[16], vhi[16];
+        float ma = 0.f, mbx = 0.f;
+        // read r of the iteration: K fragment r (r < 16), else half (r - 16) % 2
+        // of V^T fragment (r - 16) / 2
+        auto issue = [&](auto R_) __attribute__((always_inline)) {
+          constexpr int r = decltype(R_)::value;
+          if constexpr (r < 16) {
+            kf[r] = read_b128<G::koff(SK) + (r % 2) * 32 * G::RB>(kaddr[r / 2]);
+          } else {
+            constexpr int k = (r - 16) / 2, half = (r - 16) % 2, t2 = k / 4, e = k % 4;
+            const bf16x4 x = read_tr16<G::voff(SV) + (16 * t2 + 8 * half) * G::RB>(vaddr[e]);
+            if constexpr (half) vhi[k] = x; else vlo[k] = x;
+          }
+        };
+        static_for<32>([&](auto S_) __attribute__((always_inline)) {
+          constexpr int s = decltype(S_)::value;
+          if constexpr (s == 0) {
+            static_for<fpipe::kLook + 1>([&](auto K_) __attribute__((always_inline)) {
+              issue(IC<decltype(K_)::value>{});
+            });
+          }
+          constexpr int W = fpipe::issued(s - 1) - fpipe::need(s);
+          static_assert(W >= 0 && W <= 15, "wait count");
+          if constexpr (s < 16) {
+            constexpr int t = s / 2, jb = s % 2;
+            wait_lds<W>(kf[s]);
+            nxt[jb] = mfma_bf16(kf[s], qf[t], t == 0 ? f32x16{} : nxt[jb]);
+          } else {
+            constexpr int k = s - 16, t2 = k / 4, e = k % 4;
+            asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(vlo[k]), "+v"(vhi[k]) : "n"(W));
+            const bf16x8 vf = bf16x8{vlo[k][0], vlo[k][1], vlo[k][2], vlo[k][3],
+                                     vhi[k][0], vhi[k][1], vhi[k][2], vhi[k][3]};
+            const bf16x8 pb = __builtin_bit_cast(
+                bf16x8, i32x4{(int)pw[4 * t2], (int)pw[4 * t2 + 1], (int)pw[4 * t2 + 2],
+                              (int)pw[4 * t2 + 3]});
+            oacc[e] = mfma_bf16(vf, pb, oacc[e]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          constexpr int first = fpipe::issued(s - 1) + 1;
+          static_for<fpipe::issued(s) - fpipe::issued(s - 1)>([&](auto K_) __attribute__((always_inline)) {
+            issue(IC<first + decltype(K_)::value>{});
+          });
+          static_for<32>([&](auto E_) __attribute__((always_inline)) {
+            constexpr int v = decltype(E_)::value;
+            if constexpr (fpipe::exp_slot(v) == s) {
+              constexpr int t2 = v / 8, sl = v % 8;
+              pe[v] = exp2_fast(__builtin_fmaf(cur[t2 >> 1][8 * (t2 & 1) + sl], scale_log2, neg_m));
+              rsum += pe[v];
+              if constexpr (v % 2 == 1) {
+                pw[v / 2] = pack_bf16x2(pe[v - 1], pe[v]);
+                asm volatile("" : "+v"(rsum), "+v"(pw[v / 2]));
+              } else {
+                asm volatile("" : "+v"(rsum), "+v"(pe[v]));
+              }
+            }
+          });
+          if constexpr (s >= 24) {
+            constexpr int r = 2 * (s - 24);
+            if constexpr (s == 24) {
+              ma = fmaxf(nxt[0][0], nxt[0][1]);
+              mbx = fmaxf(nxt[1][0], nxt[1][1]);
+            } else {
+              ma = fmaxf(ma, fmaxf(nxt[0][r], nxt[0][r + 1]));
+              mbx = fmaxf(mbx, fmaxf(nxt[1][r], nxt[1][r + 1]));
+            }
+            asm volatile("" : "+v"(ma), "+v"(mbx));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        l += rsum;
+        mx = max_halves(fmaxf(ma, mbx));
+      };
+      for (int j = 0; j + 2 < nint - 1; j += 2) {
+        iter(IC<1>{}, IC<0>{}, sA, sB, j);
+        iter(IC<0>{}, IC<1>{}, sB, sA, j + 1);
+      }
+      iter(IC<1>{}, IC<0>{}, sA, sB, nint - 2);
+      // The last interior tile's P.V: V(nint-1) in V slot 1, S(nint-1) in sB.
+      {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        bf16x8 vf[4][4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int t2 = 0; t2 < 4; ++t2) {
+            const bf16x4 lo = read_tr16<0>(vaddr[e] + G::voff(1) + 16 * t2 * G::RB);
+            const bf16x4 hi = read_tr16<0>(vaddr[e] + G::voff(1) + (16 * t2 + 8) * G::RB);
+            vf[t2][e] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
+        raise_offset(mx);
+        const float neg_m = -m;
+        float rsum = 0.f;
+        bf16x8 pb[4];
+#pragma unroll
+        for (int t2 = 0; t2 < 4; ++t2)
+#pragma unroll
+          for (int sl = 0; sl < 8; ++sl) {
+            const float pv =
+                exp2_fast(__builtin_fmaf(sB[t2 >> 1][8 * (t2 & 1) + sl], scale_log2, neg_m));
+            rsum += pv;
+            pb[t2][sl] = (__bf16)pv;
+          }
+        l += rsum;
+        lds_wait_v(vf);
+#pragma unroll
+        for (int t2 = 0; t2 < 4; ++t2)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) oacc[e] = mfma_bf16(vf[t2][e], pb[t2], oacc[e]);
+      }
+      kb = nint;
+      __syncthreads();  // every wave is done with both stages
+    }
+  }
+  if (kb < nkb) LOAD_TILE(0, kb * kBC);
   for (; kb < nkb_int; kb += 2) {
     STEP(0, kb, false);
     STEP(1, kb + 1, false);
@@ -341,7 +559,7 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
 // (heavier block of a unit first).  With xcd_remap the units of one head stay
 // on one XCD.  Causal, nunits == 0: one workgroup per query block, heaviest
 // first, dispatched by the hardware as CUs free up.
-template <int D, bool CAUSAL, int NW>
+template <int D, bool CAUSAL, int NW, bool PIPE>
 __global__ __launch_bounds__(64 * NW, D > 128 ? 1 : 2) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int H, int Hkv, int N, float scale_log2,
@@ -367,7 +585,7 @@ __global__ __launch_bounds__(64 * NW, D > 128 ? 1 : 2) void attn_fwd_bf16_kernel
       bh = L / nqb;
       qb = L % nqb;
     }
-    attend_block<D, CAUSAL, NW>(smem, Q, K, V, O, LSE, H, Hkv, N, scale_log2, bh,
+    attend_block<D, CAUSAL, NW, PIPE>(smem, Q, K, V, O, LSE, H, Hkv, N, scale_log2, bh,
                                 CAUSAL ? nqb - 1 - qb : qb);
   } else {
     // One call site for both causal modes (a second inlined copy of the
@@ -397,7 +615,7 @@ __global__ __launch_bounds__(64 * NW, D > 128 ? 1 : 2) void attn_fwd_bf16_kernel
       } else {
         qblk = nqb - 1 - item;
       }
-      attend_block<D, CAUSAL, NW>(smem, Q, K, V, O, LSE, H, Hkv, N, scale_log2, bh, qblk);
+      attend_block<D, CAUSAL, NW, PIPE>(smem, Q, K, V, O, LSE, H, Hkv, N, scale_log2, bh, qblk);
       if (last) {
         second = 0;
         s += gridDim.x;
@@ -409,7 +627,7 @@ __global__ __launch_bounds__(64 * NW, D > 128 ? 1 : 2) void attn_fwd_bf16_kernel
   }
 }
 
-template <int D, bool CAUSAL, int NW>
+template <int D, bool CAUSAL, int NW, bool PIPE>
 hipError_t launch_nw(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                      int Hkv, int N, float scale, hipStream_t stream) {
   constexpr int kBR = 32 * NW;
@@ -420,7 +638,7 @@ hipError_t launch_nw(const void* q, const void* k, const void* v, void* o, float
     const int64_t units = (int64_t)B * H * ((nqb + 1) / 2);
     static std::atomic<int> resident{0};
     const int ncu = current_cu_count();
-    const int per_cu = resident_per_cu(attn_fwd_bf16_kernel<D, CAUSAL, NW>, 64 * NW, resident);
+    const int per_cu = resident_per_cu(attn_fwd_bf16_kernel<D, CAUSAL, NW, PIPE>, 64 * NW, resident);
     if (ncu <= 0 || per_cu <= 0) return hipErrorInvalidDevice;
     // At most two slots per CU: at d = 64 three 4-wave workgroups fit, but a
     // third slot per CU measured 2-8% slower on most causal shapes.
@@ -438,7 +656,7 @@ hipError_t launch_nw(const void* q, const void* k, const void* v, void* o, float
   // the K/V head groups (B * Hkv of them) split evenly over the 8 XCDs, and a
   // persistent grid a multiple of 8 (each slot stays on one XCD)
   const int remap = (((int64_t)B * Hkv) % 8 == 0 && grid % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, NW>), dim3((unsigned)grid), dim3(64 * NW), 0,
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, NW, PIPE>), dim3((unsigned)grid), dim3(64 * NW), 0,
                      stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse,
                      H, Hkv, N, scale * kLog2e, nqb, remap, (int)nunits);
   return hipGetLastError();
@@ -448,17 +666,18 @@ hipError_t launch_nw(const void* q, const void* k, const void* v, void* o, float
 // sequences) or the causal work is uneven; crossover measured on the 16384-
 // token sweep (B = 16384 / N): N <= 1024 (d=128) / 2048 (d=64) non-causal,
 // N <= 4096 / 8192 causal.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PIPE = false>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                   int Hkv, int N, float scale, hipStream_t stream) {
   // d = 256: one wave per SIMD (Q fragments and O take 192 registers), so
   // always four waves.
   if constexpr (D > 128) {
-    return launch_nw<D, CAUSAL, 4>(q, k, v, o, lse, B, H, Hkv, N, scale, stream);
+    return launch_nw<D, CAUSAL, 4, false>(q, k, v, o, lse, B, H, Hkv, N, scale, stream);
   } else {
     const int small_n = (CAUSAL ? 4096 : 1024) * (128 / D);
-    if (N <= small_n) return launch_nw<D, CAUSAL, 4>(q, k, v, o, lse, B, H, Hkv, N, scale, stream);
-    return launch_nw<D, CAUSAL, 8>(q, k, v, o, lse, B, H, Hkv, N, scale, stream);
+    if (N <= small_n)
+      return launch_nw<D, CAUSAL, 4, false>(q, k, v, o, lse, B, H, Hkv, N, scale, stream);
+    return launch_nw<D, CAUSAL, 8, PIPE>(q, k, v, o, lse, B, H, Hkv, N, scale, stream);
   }
 }
 
@@ -466,7 +685,11 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
 
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                                 int B, int H, int Hkv, int N, int d, bool causal,
-                                float softmax_scale, hipStream_t stream) {
+                                float softmax_scale, hipStream_t stream, bool pipelined) {
+  // The pipelined schedule exists for d = 128 non-causal (8-wave workgroups);
+  // every other case runs the same-phase kernel, whose results it equals.
+  if (pipelined && d == 128 && !causal)
+    return launch<128, false, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream);
   if (d == 256)
     return causal ? launch<256, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream)
                   : launch<256, false>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream);

@@ -82,6 +82,22 @@ int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* l
                   int B, int H, int N, int d, int causal, float softmax_scale, void* stream);
 
 /*
+ * attn_fwd_bf16 with the intra-wave pipelined schedule of the FlashAttention-3
+ * report, section 3.2: each wave issues the matrix products of S(j+1) = Q
+ * K(j+1)^T and of O += P(j) V(j) one at a time between the exponentials and
+ * sums of block j's softmax, so that the matrix cores work while the softmax
+ * runs.  Arguments, validation, errors and results are those of
+ * attn_fwd_bf16, bit for bit.  The schedule applies to d = 128 non-causal
+ * with N > 1024 (where the library runs 8-wave workgroups); every other case
+ * runs the attn_fwd_bf16 kernel.  On MI355X it measures about as fast as
+ * attn_fwd_bf16's same-phase schedule (see the bench line's pipelined leg),
+ * which stays the default.
+ */
+int attn_fwd_bf16_pipelined(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int N, int d, int causal, float softmax_scale,
+                            void* stream);
+
+/*
  * FP8 (OCP e4m3) attention forward, FlashAttention-3 report section 3.3.
  *   q8, k8, v8   e4m3 codes, BSHD (one byte per element), as written by
  *                blockquant_hadamard (Q and K rotated with the same signs).

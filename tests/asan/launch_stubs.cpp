@@ -10,7 +10,7 @@
 namespace exattn {
 
 hipError_t launch_attn_fwd_bf16(const void*, const void*, const void*, void*, float*, int, int, int,
-                                int, int, bool, float, hipStream_t) {
+                                int, int, bool, float, hipStream_t, bool) {
   return hipErrorNoDevice;
 }
 hipError_t launch_attn_fwd_fp8(const void*, const void*, const void*, const float*, const float*,
