@@ -65,7 +65,7 @@ def parse():
     p.add_argument("--causal-reps", type=int, default=20,
                    help="launches of the causal forwards on the same workloads (0: skip)")
     p.add_argument("--pipe-reps", type=int, default=20,
-                   help="launches of the pipelined bf16 schedule and the same-phase kernel, "
+                   help="launches of attn_fwd_bf16 (pipelined) and attn_fwd_bf16_same_phase, "
                         "alternated, at the bf16 workload and B4 H16 N4096 (0: skip)")
     p.add_argument("--d256-reps", type=int, default=20,
                    help="launches of the head-dim-256 forwards, B2 H8 N8192 (0: skip)")
@@ -460,10 +460,11 @@ def main():
                              "ms": round(t_c8 * 1e3, 4)},
             "finite": bool(torch.isfinite(o16).all().item() and torch.isfinite(o8).all().item())}
     if a.pipe_reps > 0 and not a.causal and a.d == 128:
-        # The intra-wave pipelined schedule (attn_fwd_bf16_pipelined) against
-        # the same-phase kernel on the same inputs, alternated twice; the two
-        # must agree bit for bit.
-        print(f"[bench] pipelined schedule: {a.pipe_reps} launches x 2 rounds", file=sys.stderr,
+        # The two schedules of the bf16 forward on the same inputs, alternated
+        # twice: attn_fwd_bf16 (the intra-wave pipelined loop at d = 128
+        # non-causal) against attn_fwd_bf16_same_phase.  They must agree bit
+        # for bit.
+        print(f"[bench] schedules: {a.pipe_reps} launches x 2 rounds", file=sys.stderr,
               flush=True)
         legs = {}
         for name, (Bp, Np) in (("headline", (B, N)), ("b4n4096", (4, 4096))):
@@ -474,19 +475,20 @@ def main():
                 qp, kp, vp = (dev_bf16(x) for x in workloads.gen_qkv(wp))
             op, lp = torch.empty_like(qp), torch.empty((Bp, H, Np), dtype=torch.float32, device=dev)
             op2, lp2 = torch.empty_like(op), torch.empty_like(lp)
-            plain = lambda: ea.attn_fwd_bf16(qp, kp, vp, softmax_scale=scale, out=op, lse=lp)
-            piped = lambda: ea.attn_fwd_bf16_pipelined(qp, kp, vp, softmax_scale=scale, out=op2,
+            piped = lambda: ea.attn_fwd_bf16(qp, kp, vp, softmax_scale=scale, out=op, lse=lp)
+            same = lambda: ea.attn_fwd_bf16_same_phase(qp, kp, vp, softmax_scale=scale, out=op2,
                                                        lse=lp2)
-            tp, tq = [], []
+            tp, ts = [], []
             for _ in range(2):
-                tp.append(time_reps(plain, a.pipe_reps, stream))
-                tq.append(time_reps(piped, a.pipe_reps, stream))
+                tp.append(time_reps(piped, a.pipe_reps, stream))
+                ts.append(time_reps(same, a.pipe_reps, stream))
             f = wp.flops()
             legs[name] = {"workload": wp.name,
-                          "same_phase": round(f / min(tp) / 1e12, 2),
-                          "pipelined": round(f / min(tq) / 1e12, 2),
+                          "pipelined": round(f / min(tp) / 1e12, 2),
+                          "same_phase": round(f / min(ts) / 1e12, 2),
                           "bit_identical": bool(torch.equal(op, op2) and torch.equal(lp, lp2))}
-        out["pipelined"] = {"kernel": "attn_fwd_bf16_pipelined", "unit": "TFLOP/s",
+        out["schedules"] = {"kernels": "attn_fwd_bf16 (pipelined) vs attn_fwd_bf16_same_phase",
+                            "unit": "TFLOP/s",
                             "timing": "best of two medians of per-call HIP event times, alternated",
                             **legs}
     if a.d256_reps > 0:

@@ -10,8 +10,8 @@ Entry points (same names as the C ABI):
   attn_fwd_bf16(q, k, v, causal=False, softmax_scale=None) -> (o, lse)
   blockquant_hadamard(x, signs=None, block_rows=128) -> (x8, scale)
   attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal=False, softmax_scale=None) -> (o, lse)
-  attn_fwd_bf16_pipelined(q, k, v, causal=False, softmax_scale=None) -> (o, lse): the same
-    results from the intra-wave pipelined schedule
+  attn_fwd_bf16_same_phase(q, k, v, causal=False, softmax_scale=None) -> (o, lse): the same
+    results from the same-phase schedule (attn_fwd_bf16 pipelines d = 128 non-causal)
   attn_fwd_bf16_gqa / attn_fwd_fp8_gqa: the same with K/V (and their scales) on
     H_kv heads, H a multiple of H_kv (grouped-query / multi-query attention).
   attn_bwd_bf16(q, k, v, o, lse, do, causal=False, softmax_scale=None) -> (dq, dk, dv)
@@ -35,7 +35,7 @@ _c_float = ctypes.c_float
 # (name, argtypes) for every symbol of include/exattn.h
 SIGNATURES = {
     "attn_fwd_bf16": [_c_void_p] * 5 + [_c_int] * 5 + [_c_float, _c_void_p],
-    "attn_fwd_bf16_pipelined": [_c_void_p] * 5 + [_c_int] * 5 + [_c_float, _c_void_p],
+    "attn_fwd_bf16_same_phase": [_c_void_p] * 5 + [_c_int] * 5 + [_c_float, _c_void_p],
     "attn_fwd_fp8": [_c_void_p] * 8 + [_c_int] * 5 + [_c_float, _c_void_p],
     "attn_fwd_bf16_gqa": [_c_void_p] * 5 + [_c_int] * 6 + [_c_float, _c_void_p],
     "attn_fwd_fp8_gqa": [_c_void_p] * 8 + [_c_int] * 6 + [_c_float, _c_void_p],
@@ -165,11 +165,11 @@ def attn_fwd_bf16(q, k, v, causal: bool = False, softmax_scale: float | None = N
     return _bf16("attn_fwd_bf16", q, k, v, causal, softmax_scale, out, lse)
 
 
-def attn_fwd_bf16_pipelined(q, k, v, causal: bool = False, softmax_scale: float | None = None,
-                            out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
-    """attn_fwd_bf16 with the intra-wave pipelined schedule (d = 128 non-causal,
-    N > 1024; the plain kernel otherwise); results bit-identical to attn_fwd_bf16."""
-    return _bf16("attn_fwd_bf16_pipelined", q, k, v, causal, softmax_scale, out, lse)
+def attn_fwd_bf16_same_phase(q, k, v, causal: bool = False, softmax_scale: float | None = None,
+                             out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """attn_fwd_bf16 with the same-phase schedule everywhere (attn_fwd_bf16
+    pipelines d = 128 non-causal, N > 1024); results bit-identical to it."""
+    return _bf16("attn_fwd_bf16_same_phase", q, k, v, causal, softmax_scale, out, lse)
 
 
 def attn_fwd_bf16_gqa(q, k, v, causal: bool = False, softmax_scale: float | None = None,

@@ -67,7 +67,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? EXATTN_OK : EXATTN_ERR_H
 
 extern "C" {
 
-int exattn_abi_version(void) { return 8; }
+int exattn_abi_version(void) { return 9; }
 
 const char* exattn_strerror(int code) {
   switch (code) {
@@ -91,7 +91,7 @@ const char* exattn_strerror(int code) {
 namespace {
 int fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
              int H_kv, int N, int d, int causal, float softmax_scale, void* stream,
-             bool pipelined) {
+             bool same_phase) {
   int rc = check_shape(B, H, N, d, 2);
   if (rc) return rc;
   if (!good_heads(H, H_kv)) return EXATTN_ERR_SHAPE;
@@ -106,7 +106,7 @@ int fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (aliased({{o, bytes}, {lse, (int64_t)B * H * N * 4}}, {{q, bytes}, {k, kv_bytes}, {v, kv_bytes}}))
     return EXATTN_ERR_VALUE;
   return hip_status(exattn::launch_attn_fwd_bf16(q, k, v, o, lse, B, H, H_kv, N, d, causal != 0,
-                                                 softmax_scale, (hipStream_t)stream, pipelined));
+                                                 softmax_scale, (hipStream_t)stream, same_phase));
 }
 }  // namespace
 
@@ -121,9 +121,9 @@ int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* l
   return fwd_bf16(q, k, v, o, lse, B, H, H, N, d, causal, softmax_scale, stream, false);
 }
 
-int attn_fwd_bf16_pipelined(const void* q, const void* k, const void* v, void* o, float* lse,
-                            int B, int H, int N, int d, int causal, float softmax_scale,
-                            void* stream) {
+int attn_fwd_bf16_same_phase(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int H, int N, int d, int causal, float softmax_scale,
+                             void* stream) {
   return fwd_bf16(q, k, v, o, lse, B, H, H, N, d, causal, softmax_scale, stream, true);
 }
 

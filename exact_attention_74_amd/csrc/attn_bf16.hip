@@ -11,7 +11,11 @@
 // running sum l, one final normalisation).  Causal work at d <= 128 runs on
 // persistent workgroup slots over pairs of query blocks of equal total cost
 // (see the kernel below).  Head dim 256 runs 4-wave workgroups, one wave
-// per SIMD.
+// per SIMD.  At head dim 128, non-causal, the interior key tiles of the
+// 8-wave workgroups run software-pipelined (the next tile's S MFMAs issued
+// between the current tile's exponentials, report section 3.2); every other
+// case runs the same-phase loop (both waves of a SIMD do MFMAs, then both do
+// softmax).
 //
 // Transposed formulation.  Each wave computes S^T = K Q^T (keys as MFMA rows,
 // its 32 queries as MFMA columns), so the accumulator keeps every query on one
@@ -171,8 +175,8 @@ __device__ __forceinline__ void tile_compute(const char* smem, const uint32_t (&
 #undef TR_PAIR
 }
 
-// Software-pipelined interior tiles (the pipelined entry point, head dim 128,
-// non-causal, 8-wave workgroups).  The FlashAttention-3 report (section 3.2)
+// Software-pipelined interior tiles (head dim 128, non-causal, 8-wave
+// workgroups; the same-phase loop below serves every other case).  The FlashAttention-3 report (section 3.2)
 // issues the next block's S = Q K^T before the current block's softmax so
 // that the matrix cores work while the exponentials run.  Here iteration j of
 // a wave issues 32 MFMAs as 32 slots: the 16 of S(j+1) = K(j+1) Q^T, then the
@@ -187,7 +191,7 @@ __device__ __forceinline__ void tile_compute(const char* smem, const uint32_t (&
 // element goes through the same operations in the same order as in the
 // same-phase loop, so the results are bit-identical to it.
 namespace fpipe {
-constexpr int kLook = 8;   // LDS reads in flight ahead of the MFMA that needs them
+constexpr int kLook = 5;   // LDS reads in flight ahead of the MFMA that needs them
 constexpr int kLast = 47;  // reads per iteration - 1: 16 K fragments + 32 V^T halves
 // Read index that slot s's MFMA needs last: K fragment s, or the second V^T
 // half of fragment s - 16.
@@ -425,7 +429,6 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
                               (int)pw[4 * t2 + 3]});
             oacc[e] = mfma_bf16(vf, pb, oacc[e]);
           }
-          __builtin_amdgcn_sched_barrier(0);
           constexpr int first = fpipe::issued(s - 1) + 1;
           static_for<fpipe::issued(s) - fpipe::issued(s - 1)>([&](auto K_) __attribute__((always_inline)) {
             issue(IC<first + decltype(K_)::value>{});
@@ -455,6 +458,8 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
             }
             asm volatile("" : "+v"(ma), "+v"(mbx));
           }
+          // one fence per slot, at its end: a second one between the MFMA and
+          // the reads measured 2% slower
           __builtin_amdgcn_sched_barrier(0);
         });
         l += rsum;
@@ -685,10 +690,11 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
 
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                                 int B, int H, int Hkv, int N, int d, bool causal,
-                                float softmax_scale, hipStream_t stream, bool pipelined) {
-  // The pipelined schedule exists for d = 128 non-causal (8-wave workgroups);
-  // every other case runs the same-phase kernel, whose results it equals.
-  if (pipelined && d == 128 && !causal)
+                                float softmax_scale, hipStream_t stream, bool same_phase) {
+  // d = 128 non-causal runs the pipelined loop on its 8-wave workgroups (the
+  // same results as the same-phase loop, measured 1-3% faster); same_phase
+  // selects the same-phase loop there too, for comparison.
+  if (!same_phase && d == 128 && !causal)
     return launch<128, false, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream);
   if (d == 256)
     return causal ? launch<256, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream)

@@ -47,7 +47,7 @@ inline int resident_per_cu(K kernel, int threads, std::atomic<int>& cache) {
 // Hkv: K/V heads (H a multiple of it); query head h reads K/V head h / (H / Hkv).
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                                 int B, int H, int Hkv, int N, int d, bool causal,
-                                float softmax_scale, hipStream_t stream, bool pipelined = false);
+                                float softmax_scale, hipStream_t stream, bool same_phase = false);
 
 hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* sq,
                                const float* sk, const float* sv, void* o, float* lse, int B, int H,

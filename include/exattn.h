@@ -76,26 +76,30 @@ extern "C" {
  *   causal       0 or 1.
  *   softmax_scale  multiplies Q K^T; finite and > 0 (usually 1/sqrt(d)).
  * The score matrix is never materialised: each workgroup owns a block of
- * query rows of one (b, h) and streams K/V blocks through LDS.
+ * query rows of one (b, h) and streams K/V blocks through LDS; at d = 128,
+ * non-causal, N > 1024, each wave software-pipelines the matrix products of
+ * the next key block under the softmax of the current one (report section
+ * 3.2; see attn_fwd_bf16_same_phase).
  */
 int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                   int B, int H, int N, int d, int causal, float softmax_scale, void* stream);
 
 /*
- * attn_fwd_bf16 with the intra-wave pipelined schedule of the FlashAttention-3
- * report, section 3.2: each wave issues the matrix products of S(j+1) = Q
- * K(j+1)^T and of O += P(j) V(j) one at a time between the exponentials and
- * sums of block j's softmax, so that the matrix cores work while the softmax
- * runs.  Arguments, validation, errors and results are those of
- * attn_fwd_bf16, bit for bit.  The schedule applies to d = 128 non-causal
- * with N > 1024 (where the library runs 8-wave workgroups); every other case
- * runs the attn_fwd_bf16 kernel.  On MI355X it measures about as fast as
- * attn_fwd_bf16's same-phase schedule (see the bench line's pipelined leg),
- * which stays the default.
+ * attn_fwd_bf16 with the same-phase schedule everywhere: both waves of a SIMD
+ * issue a key tile's matrix products, then both run its softmax, one barrier
+ * per tile.  attn_fwd_bf16 (and attn_fwd_bf16_gqa) use this schedule except
+ * at d = 128 non-causal with N > 1024, where they run the intra-wave
+ * pipelined schedule of the FlashAttention-3 report, section 3.2: each wave
+ * issues the matrix products of S(j+1) = Q K(j+1)^T and of O += P(j) V(j) one
+ * at a time between the exponentials and sums of block j's softmax.  The two
+ * schedules compute every output element with the same operations in the
+ * same order, so the results are identical bit for bit; this entry point
+ * exists to compare them (the bench line's schedule leg).  Arguments,
+ * validation and errors as in attn_fwd_bf16.
  */
-int attn_fwd_bf16_pipelined(const void* q, const void* k, const void* v, void* o, float* lse,
-                            int B, int H, int N, int d, int causal, float softmax_scale,
-                            void* stream);
+int attn_fwd_bf16_same_phase(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int H, int N, int d, int causal, float softmax_scale,
+                             void* stream);
 
 /*
  * FP8 (OCP e4m3) attention forward, FlashAttention-3 report section 3.3.

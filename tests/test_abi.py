@@ -31,12 +31,12 @@ def _codes():
 
 def test_library_builds_and_loads():
     assert os.path.exists(ea.LIB_PATH)
-    assert ea.lib().exattn_abi_version() == 8
+    assert ea.lib().exattn_abi_version() == 9
 
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert set(names) == {"attn_fwd_bf16", "attn_fwd_bf16_pipelined", "attn_fwd_fp8",
+    assert set(names) == {"attn_fwd_bf16", "attn_fwd_bf16_same_phase", "attn_fwd_fp8",
                           "attn_fwd_bf16_gqa", "attn_fwd_fp8_gqa",
                           "attn_bwd_bf16", "attn_bwd_bf16_gqa", "attn_bwd_bf16_workspace_bytes",
                           "attn_bwd_bf16_noalloc",
@@ -66,9 +66,9 @@ def _bf16(q=P, k=P + P2, v=P + 2 * P2, o=P + 3 * P2, lse=P + 4 * P2, B=1, H=2, N
     return ea.lib().attn_fwd_bf16(q, k, v, o, lse, B, H, N, d, causal, scale, None)
 
 
-def _bf16p(q=P, k=P + P2, v=P + 2 * P2, o=P + 3 * P2, lse=P + 4 * P2, B=1, H=2, N=256, d=64,
+def _bf16s(q=P, k=P + P2, v=P + 2 * P2, o=P + 3 * P2, lse=P + 4 * P2, B=1, H=2, N=256, d=64,
            causal=0, scale=0.125):
-    return ea.lib().attn_fwd_bf16_pipelined(q, k, v, o, lse, B, H, N, d, causal, scale, None)
+    return ea.lib().attn_fwd_bf16_same_phase(q, k, v, o, lse, B, H, N, d, causal, scale, None)
 
 
 def _fp8(q=P, k=P + P2, v=P + 2 * P2, sq=P + 3 * P2, sk=P + 4 * P2, sv=P + 5 * P2, o=P + 6 * P2,
@@ -93,7 +93,7 @@ def _bq(x=P, x8=P + P2, s=P + 2 * P2, signs=None, B=1, H=2, N=256, d=64, br=128)
     return ea.lib().blockquant_hadamard(x, x8, s, signs, B, H, N, d, br, None)
 
 
-@pytest.mark.parametrize("fn", [_bf16, _bf16p, _fp8, _bf16g, _fp8g])
+@pytest.mark.parametrize("fn", [_bf16, _bf16s, _fp8, _bf16g, _fp8g])
 def test_attention_validation(fn):
     assert fn(q=None) == ea.ERR_NULL
     assert fn(o=None) == ea.ERR_NULL

@@ -35,7 +35,7 @@ CHILD = textwrap.dedent(r'''
             print(f"FAIL {what}: {got} != {want}", flush=True)
             sys.exit(3)
     # forwards (B1 H2 N256 d64): valid -> stub, then each error class
-    for fn, nptr in ((lib.attn_fwd_bf16, 5), (lib.attn_fwd_bf16_pipelined, 5), (lib.attn_fwd_fp8, 8)):
+    for fn, nptr in ((lib.attn_fwd_bf16, 5), (lib.attn_fwd_bf16_same_phase, 5), (lib.attn_fwd_fp8, 8)):
         ptrs = [P + i * G for i in range(nptr)]
         call = lambda p=ptrs, B=1, H=2, N=256, d=64, c=0, s=0.125: fn(*p, B, H, N, d, c, s, None)
         expect(call(), HIP, "valid forward")
@@ -82,7 +82,7 @@ CHILD = textwrap.dedent(r'''
     expect(lib.rope_blockquant_hadamard(*r, 2, 1, 2, 130, 64, 128, None), VALUE, "rope pairing 2")
     for code in range(-7, 1):
         expect(isinstance(lib.exattn_strerror(code), bytes), True, "strerror")
-    expect(lib.exattn_abi_version(), 8, "abi version")
+    expect(lib.exattn_abi_version(), 9, "abi version")
     print(f"ASAN_CHECKS_OK {checks}", flush=True)
 ''')
 

@@ -264,24 +264,25 @@ def test_d256_full_size_sampled_rows(causal):
     _check(rows_of(o, rows), lse_rows(lse, rows), o_ref, l_ref, w.name, absv)
 
 
-def _pipelined_vs_plain(dev, causal, scale):
-    o, lse = ea.attn_fwd_bf16_pipelined(*dev, causal=causal, softmax_scale=scale)
-    o0, lse0 = ea.attn_fwd_bf16(*dev, causal=causal, softmax_scale=scale)
+def _default_vs_same_phase(dev, causal, scale):
+    o, lse = ea.attn_fwd_bf16(*dev, causal=causal, softmax_scale=scale)
+    o0, lse0 = ea.attn_fwd_bf16_same_phase(*dev, causal=causal, softmax_scale=scale)
     torch.cuda.synchronize()
-    assert torch.equal(o, o0) and torch.equal(lse, lse0), "pipelined schedule differs"
+    assert torch.equal(o, o0) and torch.equal(lse, lse0), "the two schedules differ"
     return to_np(o), lse.cpu().numpy().astype(np.float64)
 
 
 @pytest.mark.parametrize("N", [1025, 1088, 1100, 1500, 2048])
 def test_pipelined_full_parity(N):
-    """The pipelined schedule (S(j+1) MFMAs between the exponentials of tile j;
-    d = 128 non-causal, N > 1024): every element against the oracle, and the
-    outputs bit-identical to attn_fwd_bf16's.  N = 1088 leaves an odd whole
-    tile after the pipelined pairs, the others a ragged tail of 1 to 63 keys."""
+    """The pipelined loop (S(j+1) MFMAs between the exponentials of tile j),
+    which attn_fwd_bf16 runs at d = 128 non-causal, N > 1024: every element
+    against the oracle, and the outputs bit-identical to the same-phase
+    schedule's.  N = 1088 leaves an odd whole tile after the pipelined pairs,
+    the others a ragged tail of 1 to 63 keys."""
     w = workloads.Workload(f"pipe_n{N}", 1, 3, N, 128, False, seed=41 + N)
     say(w.name)
     host, dev = bf16_inputs(w)
-    o, lse = _pipelined_vs_plain(dev, False, w.softmax_scale)
+    o, lse = _default_vs_same_phase(dev, False, w.softmax_scale)
     o_ref, lse_ref = oracle.naive_attention(*host, w.softmax_scale, False)
     absv, _ = oracle.naive_attention(host[0], host[1], np.abs(host[2]), w.softmax_scale, False)
     _check(o, lse, o_ref, lse_ref, w.name, absv)
@@ -290,14 +291,15 @@ def test_pipelined_full_parity(N):
 @pytest.mark.parametrize("B,H,N,d,causal", [(2, 16, 8192, 128, False), (1, 4, 1024, 128, False),
                                             (1, 3, 3000, 64, False), (1, 3, 3000, 128, True),
                                             (1, 2, 700, 256, False), (2, 2, 1, 128, False)])
-def test_pipelined_sampled_rows(B, H, N, d, causal):
+def test_schedules_sampled_rows(B, H, N, d, causal):
     """The bench shape B2 H16 N8192 through the pipelined loop (sampled rows
-    against the oracle), and the shapes the schedule leaves to the plain
-    kernel (short N, d = 64, causal, d = 256, one token): bit-identical."""
-    w = workloads.Workload(f"pipe_b{B}h{H}n{N}d{d}", B, H, N, d, causal, seed=7 + N)
+    against the oracle), and the shapes that run the same-phase loop under
+    both entry points (short N, d = 64, causal, d = 256, one token):
+    bit-identical."""
+    w = workloads.Workload(f"sched_b{B}h{H}n{N}d{d}", B, H, N, d, causal, seed=7 + N)
     say(w.name + ("_causal" if causal else ""))
     host, dev = bf16_inputs(w)
-    o, lse = _pipelined_vs_plain(dev, causal, w.softmax_scale)
+    o, lse = _default_vs_same_phase(dev, causal, w.softmax_scale)
     rows = workloads.sample_rows(B, H, N, 256, seed=N)
     o_ref, l_ref = oracle.naive_attention_rows(*host, w.softmax_scale, causal, rows)
     absv, _ = oracle.naive_attention_rows(host[0], host[1], np.abs(host[2]), w.softmax_scale,
