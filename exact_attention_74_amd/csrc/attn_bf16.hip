@@ -11,8 +11,8 @@
 // running sum l, one final normalisation).  Causal work at d <= 128 runs on
 // persistent workgroup slots over pairs of query blocks of equal total cost
 // (see the kernel below).  Head dim 256 runs 4-wave workgroups, one wave
-// per SIMD.  At head dim 128, non-causal, the interior key tiles of the
-// 8-wave workgroups run software-pipelined (the next tile's S MFMAs issued
+// per SIMD.  At head dim 128 the interior key tiles of the 8-wave workgroups
+// run software-pipelined (the next tile's S MFMAs issued
 // between the current tile's exponentials, report section 3.2); every other
 // case runs the same-phase loop (both waves of a SIMD do MFMAs, then both do
 // softmax).
@@ -175,8 +175,9 @@ __device__ __forceinline__ void tile_compute(const char* smem, const uint32_t (&
 #undef TR_PAIR
 }
 
-// Software-pipelined interior tiles (head dim 128, non-causal, 8-wave
-// workgroups; the same-phase loop below serves every other case).  The FlashAttention-3 report (section 3.2)
+// Software-pipelined interior tiles (head dim 128, 8-wave workgroups, both
+// masks: a causal block's tiles before its diagonal; the same-phase loop below
+// serves the edge tiles and every other case).  The FlashAttention-3 report (section 3.2)
 // issues the next block's S = Q K^T before the current block's softmax so
 // that the matrix cores work while the exponentials run.  Here iteration j of
 // a wave issues 32 MFMAs as 32 slots: the 16 of S(j+1) = K(j+1) Q^T, then the
@@ -317,7 +318,7 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
                                            hh, scale_log2);                                     \
   } while (0)
   int kb = 0;
-  if constexpr (PIPE && D == 128 && !CAUSAL && NW == 8) {
+  if constexpr (PIPE && D == 128 && NW == 8) {
     // The pipelined loop over the interior tiles 0 .. nkb_int - 1 (an even
     // count, at least two; the edge tiles follow in the loops below).  LDS:
     // K(j) sits in K slot j % 2 and V(j) in V slot j % 2 of the two stages,
@@ -691,11 +692,12 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                                 int B, int H, int Hkv, int N, int d, bool causal,
                                 float softmax_scale, hipStream_t stream, bool same_phase) {
-  // d = 128 non-causal runs the pipelined loop on its 8-wave workgroups (the
-  // same results as the same-phase loop, measured 1-3% faster); same_phase
-  // selects the same-phase loop there too, for comparison.
-  if (!same_phase && d == 128 && !causal)
-    return launch<128, false, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream);
+  // d = 128 runs the pipelined loop on its 8-wave workgroups (the same
+  // results as the same-phase loop, measured 1-4% faster, both masks);
+  // same_phase selects the same-phase loop there too, for comparison.
+  if (!same_phase && d == 128)
+    return causal ? launch<128, true, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream)
+                  : launch<128, false, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream);
   if (d == 256)
     return causal ? launch<256, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream)
                   : launch<256, false>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream);

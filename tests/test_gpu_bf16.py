@@ -288,13 +288,15 @@ def test_pipelined_full_parity(N):
     _check(o, lse, o_ref, lse_ref, w.name, absv)
 
 
-@pytest.mark.parametrize("B,H,N,d,causal", [(2, 16, 8192, 128, False), (1, 4, 1024, 128, False),
+@pytest.mark.parametrize("B,H,N,d,causal", [(2, 16, 8192, 128, False), (2, 4, 8192, 128, True),
+                                            (1, 3, 5000, 128, True), (1, 4, 1024, 128, False),
                                             (1, 3, 3000, 64, False), (1, 3, 3000, 128, True),
                                             (1, 2, 700, 256, False), (2, 2, 1, 128, False)])
 def test_schedules_sampled_rows(B, H, N, d, causal):
-    """The bench shape B2 H16 N8192 through the pipelined loop (sampled rows
-    against the oracle), and the shapes that run the same-phase loop under
-    both entry points (short N, d = 64, causal, d = 256, one token):
+    """The bench shape B2 H16 N8192 and causal N = 5000, 8192 through the
+    pipelined loop (sampled rows against the oracle; causal blocks run it up
+    to their diagonal), and the shapes that run the same-phase loop under both
+    entry points (short N, d = 64, causal N <= 4096, d = 256, one token):
     bit-identical."""
     w = workloads.Workload(f"sched_b{B}h{H}n{N}d{d}", B, H, N, d, causal, seed=7 + N)
     say(w.name + ("_causal" if causal else ""))
