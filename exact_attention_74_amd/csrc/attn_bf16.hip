@@ -11,8 +11,8 @@
 // running sum l, one final normalisation).  Causal work at d <= 128 runs on
 // persistent workgroup slots over pairs of query blocks of equal total cost
 // (see the kernel below).  Head dim 256 runs 4-wave workgroups, one wave
-// per SIMD.  At head dim 128 the interior key tiles of the 8-wave workgroups
-// run software-pipelined (the next tile's S MFMAs issued
+// per SIMD.  At head dims 64 and 128 the interior key tiles of the 8-wave
+// workgroups run software-pipelined (the next tile's S MFMAs issued
 // between the current tile's exponentials, report section 3.2); every other
 // case runs the same-phase loop (both waves of a SIMD do MFMAs, then both do
 // softmax).
@@ -175,34 +175,52 @@ __device__ __forceinline__ void tile_compute(const char* smem, const uint32_t (&
 #undef TR_PAIR
 }
 
-// Software-pipelined interior tiles (head dim 128, 8-wave workgroups, both
-// masks: a causal block's tiles before its diagonal; the same-phase loop below
-// serves the edge tiles and every other case).  The FlashAttention-3 report (section 3.2)
-// issues the next block's S = Q K^T before the current block's softmax so
-// that the matrix cores work while the exponentials run.  Here iteration j of
-// a wave issues 32 MFMAs as 32 slots: the 16 of S(j+1) = K(j+1) Q^T, then the
-// 16 of O^T += V(j)^T P(j)^T.  Between them run the VALU work of tile j's
-// softmax and S(j+1)'s row max (slots 24-31): exponential v (with its
-// multiply-add and row-sum add) in slot 7v / 8 of slots 0-27, about one per
-// MFMA, and each bf16 pair packed in the slot of its second exponential, so
-// every P^T operand is complete before its first MFMA (measured 0.8% faster
-// than two exponentials in each of 16 slots).  Each MFMA's K or V^T fragment is read
-// kLook reads ahead and waited for with an exact lgkmcnt count.  K is loaded
-// one tile ahead of V in the same two LDS stages (no extra LDS).  Every output
-// element goes through the same operations in the same order as in the
+// Software-pipelined interior tiles (head dims 64 and 128, 8-wave workgroups,
+// both masks: a causal block's tiles before its diagonal; the same-phase loop
+// below serves the edge tiles and every other case).  The FlashAttention-3
+// report (section 3.2) issues the next block's S = Q K^T before the current
+// block's softmax so that the matrix cores work while the exponentials run.
+// Here iteration j of a wave issues its MFMAs one per slot: the NS of
+// S(j+1) = K(j+1) Q^T, then the NP of O^T += V(j)^T P(j)^T (d = 128: 16 + 16
+// slots, d = 64: 8 + 8).  Between them run the VALU work of tile j's softmax
+// and S(j+1)'s row max (the last 8 slots): exponential v (with its multiply-
+// add and row-sum add) in slot exp_slot(v), spread evenly over the slots
+// before the last P^T operand's first MFMA (d = 128: about one per slot), and
+// each bf16 pair packed in the slot of its second exponential, so every P^T
+// operand is complete before its first MFMA (d = 128: measured 0.8% faster
+// than two exponentials in each of 16 slots).  Each MFMA's K or V^T fragment
+// is read kLook reads ahead and waited for with an exact lgkmcnt count.  K is
+// loaded one tile ahead of V in the same two LDS stages (no extra LDS).  Every
+// output element goes through the same operations in the same order as in the
 // same-phase loop, so the results are bit-identical to it.
 namespace fpipe {
-constexpr int kLook = 5;   // LDS reads in flight ahead of the MFMA that needs them
-constexpr int kLast = 47;  // reads per iteration - 1: 16 K fragments + 32 V^T halves
-// Read index that slot s's MFMA needs last: K fragment s, or the second V^T
-// half of fragment s - 16.
-constexpr int need(int s) { return s < 16 ? s : 16 + 2 * (s - 16) + 1; }
-// Reads issued by the end of slot s (s = -1: the prologue).
-constexpr int issued(int s) {
-  return s < 0 ? kLook : (need(s) + kLook < kLast ? need(s) + kLook : kLast);
-}
-// Exponential v (0 .. 31) of tile j's P^T runs in slot exp_slot(v).
-constexpr int exp_slot(int v) { return (7 * v) / 8; }
+constexpr int kLook = 5;  // LDS reads in flight ahead of the MFMA that needs them
+template <int D>
+struct Slots {
+  static constexpr int NS = 2 * (D / 16);  // S(j+1) MFMAs = K fragments
+  static constexpr int NE = D / 32;        // 32-dim blocks of O^T
+  static constexpr int NP = 4 * NE;        // P(j).V(j) MFMAs, two V^T half reads each
+  static constexpr int N = NS + NP;        // slots per iteration
+  static constexpr int kLast = NS + 2 * NP - 1;  // last read index of the iteration
+  // Read that slot s's MFMA needs last: K fragment s, or the second V^T half
+  // of P.V MFMA s - NS.
+  static constexpr int need(int s) { return s < NS ? s : NS + 2 * (s - NS) + 1; }
+  // Reads issued by the end of slot s (s = -1: the prologue).
+  static constexpr int issued(int s) {
+    return s < 0 ? kLook : (need(s) + kLook < kLast ? need(s) + kLook : kLast);
+  }
+  // Exponential v (0 .. 31) of tile j's P^T: slots 0 .. NS + 3 NE - 1.
+  static constexpr int exp_slot(int v) { return (v * (NS + 3 * NE)) / 32; }
+  // P^T operand t2 (bf16 pairs 4 t2 .. 4 t2 + 3) is first read in slot
+  // NS + t2 NE, so its last exponential must come earlier.
+  static constexpr bool exps_in_time() {
+    for (int t2 = 0; t2 < 4; ++t2)
+      if (exp_slot(8 * t2 + 7) >= NS + t2 * NE) return false;
+    return true;
+  }
+  static_assert(exps_in_time(), "an exponential after its P^T operand's first MFMA");
+  static constexpr int kMax0 = N - 8;  // S(j+1)'s row max: slots kMax0 .. N - 1
+};
 }  // namespace fpipe
 
 // One workgroup's work item: query block qblk (32 * NW rows) of head bh,
@@ -318,7 +336,8 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
                                            hh, scale_log2);                                     \
   } while (0)
   int kb = 0;
-  if constexpr (PIPE && D == 128 && NW == 8) {
+  if constexpr (PIPE && D <= 128 && NW == 8) {
+    using P = fpipe::Slots<D>;
     // The pipelined loop over the interior tiles 0 .. nkb_int - 1 (an even
     // count, at least two; the edge tiles follow in the loops below).  LDS:
     // K(j) sits in K slot j % 2 and V(j) in V slot j % 2 of the two stages,
@@ -348,7 +367,7 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
       // S(0) ahead of the loop, as in the same-phase tile body.
       f32x16 sA[2], sB[2];
       {
-        constexpr int NK = 16, AHEAD = 8;
+        constexpr int NK = P::NS, AHEAD = 8;
         bf16x8 kf[NK];
         auto rd = [&](auto I) __attribute__((always_inline)) {
           constexpr int i = decltype(I)::value, t = i / 2, j = i % 2;
@@ -392,36 +411,37 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
         float rsum = 0.f;
         uint32_t pw[16];  // P(j)^T as bf16 pairs
         float pe[32];     // its exponentials
-        bf16x8 kf[16];
-        bf16x4 vlo[16], vhi[16];
+        bf16x8 kf[P::NS];
+        bf16x4 vlo[P::NP], vhi[P::NP];
         float ma = 0.f, mbx = 0.f;
-        // read r of the iteration: K fragment r (r < 16), else half (r - 16) % 2
-        // of V^T fragment (r - 16) / 2
+        // read r of the iteration: K fragment r (r < NS), else half (r - NS) % 2
+        // of V^T fragment (r - NS) / 2
         auto issue = [&](auto R_) __attribute__((always_inline)) {
           constexpr int r = decltype(R_)::value;
-          if constexpr (r < 16) {
+          if constexpr (r < P::NS) {
             kf[r] = read_b128<G::koff(SK) + (r % 2) * 32 * G::RB>(kaddr[r / 2]);
           } else {
-            constexpr int k = (r - 16) / 2, half = (r - 16) % 2, t2 = k / 4, e = k % 4;
+            constexpr int k = (r - P::NS) / 2, half = (r - P::NS) % 2, t2 = k / P::NE,
+                          e = k % P::NE;
             const bf16x4 x = read_tr16<G::voff(SV) + (16 * t2 + 8 * half) * G::RB>(vaddr[e]);
             if constexpr (half) vhi[k] = x; else vlo[k] = x;
           }
         };
-        static_for<32>([&](auto S_) __attribute__((always_inline)) {
+        static_for<P::N>([&](auto S_) __attribute__((always_inline)) {
           constexpr int s = decltype(S_)::value;
           if constexpr (s == 0) {
             static_for<fpipe::kLook + 1>([&](auto K_) __attribute__((always_inline)) {
               issue(IC<decltype(K_)::value>{});
             });
           }
-          constexpr int W = fpipe::issued(s - 1) - fpipe::need(s);
+          constexpr int W = P::issued(s - 1) - P::need(s);
           static_assert(W >= 0 && W <= 15, "wait count");
-          if constexpr (s < 16) {
+          if constexpr (s < P::NS) {
             constexpr int t = s / 2, jb = s % 2;
             wait_lds<W>(kf[s]);
             nxt[jb] = mfma_bf16(kf[s], qf[t], t == 0 ? f32x16{} : nxt[jb]);
           } else {
-            constexpr int k = s - 16, t2 = k / 4, e = k % 4;
+            constexpr int k = s - P::NS, t2 = k / P::NE, e = k % P::NE;
             asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(vlo[k]), "+v"(vhi[k]) : "n"(W));
             const bf16x8 vf = bf16x8{vlo[k][0], vlo[k][1], vlo[k][2], vlo[k][3],
                                      vhi[k][0], vhi[k][1], vhi[k][2], vhi[k][3]};
@@ -430,13 +450,13 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
                               (int)pw[4 * t2 + 3]});
             oacc[e] = mfma_bf16(vf, pb, oacc[e]);
           }
-          constexpr int first = fpipe::issued(s - 1) + 1;
-          static_for<fpipe::issued(s) - fpipe::issued(s - 1)>([&](auto K_) __attribute__((always_inline)) {
+          constexpr int first = P::issued(s - 1) + 1;
+          static_for<P::issued(s) - P::issued(s - 1)>([&](auto K_) __attribute__((always_inline)) {
             issue(IC<first + decltype(K_)::value>{});
           });
           static_for<32>([&](auto E_) __attribute__((always_inline)) {
             constexpr int v = decltype(E_)::value;
-            if constexpr (fpipe::exp_slot(v) == s) {
+            if constexpr (P::exp_slot(v) == s) {
               constexpr int t2 = v / 8, sl = v % 8;
               pe[v] = exp2_fast(__builtin_fmaf(cur[t2 >> 1][8 * (t2 & 1) + sl], scale_log2, neg_m));
               rsum += pe[v];
@@ -448,9 +468,9 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
               }
             }
           });
-          if constexpr (s >= 24) {
-            constexpr int r = 2 * (s - 24);
-            if constexpr (s == 24) {
+          if constexpr (s >= P::kMax0) {
+            constexpr int r = 2 * (s - P::kMax0);
+            if constexpr (s == P::kMax0) {
               ma = fmaxf(nxt[0][0], nxt[0][1]);
               mbx = fmaxf(nxt[1][0], nxt[1][1]);
             } else {
@@ -475,9 +495,9 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
       {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        bf16x8 vf[4][4];
+        bf16x8 vf[4][P::NE];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+        for (int e = 0; e < P::NE; ++e)
 #pragma unroll
           for (int t2 = 0; t2 < 4; ++t2) {
             const bf16x4 lo = read_tr16<0>(vaddr[e] + G::voff(1) + 16 * t2 * G::RB);
@@ -502,7 +522,7 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
 #pragma unroll
         for (int t2 = 0; t2 < 4; ++t2)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) oacc[e] = mfma_bf16(vf[t2][e], pb[t2], oacc[e]);
+          for (int e = 0; e < P::NE; ++e) oacc[e] = mfma_bf16(vf[t2][e], pb[t2], oacc[e]);
       }
       kb = nint;
       __syncthreads();  // every wave is done with both stages
@@ -692,12 +712,15 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                                 int B, int H, int Hkv, int N, int d, bool causal,
                                 float softmax_scale, hipStream_t stream, bool same_phase) {
-  // d = 128 runs the pipelined loop on its 8-wave workgroups (the same
-  // results as the same-phase loop, measured 1-4% faster, both masks);
+  // d = 64 and 128 run the pipelined loop on their 8-wave workgroups (the
+  // same results as the same-phase loop, measured 1-4% faster, both masks);
   // same_phase selects the same-phase loop there too, for comparison.
   if (!same_phase && d == 128)
     return causal ? launch<128, true, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream)
                   : launch<128, false, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream);
+  if (!same_phase && d == 64)
+    return causal ? launch<64, true, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream)
+                  : launch<64, false, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream);
   if (d == 256)
     return causal ? launch<256, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream)
                   : launch<256, false>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream);

@@ -76,8 +76,8 @@ extern "C" {
  *   causal       0 or 1.
  *   softmax_scale  multiplies Q K^T; finite and > 0 (usually 1/sqrt(d)).
  * The score matrix is never materialised: each workgroup owns a block of
- * query rows of one (b, h) and streams K/V blocks through LDS; at d = 128,
- * N > 1024 (causal: N > 4096), each wave software-pipelines the matrix products of
+ * query rows of one (b, h) and streams K/V blocks through LDS; at d = 64 and
+ * 128 on long sequences each wave software-pipelines the matrix products of
  * the next key block under the softmax of the current one (report section
  * 3.2; see attn_fwd_bf16_same_phase).
  */
@@ -88,7 +88,8 @@ int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* l
  * attn_fwd_bf16 with the same-phase schedule everywhere: both waves of a SIMD
  * issue a key tile's matrix products, then both run its softmax, one barrier
  * per tile.  attn_fwd_bf16 (and attn_fwd_bf16_gqa) use this schedule except
- * at d = 128 with N > 1024 (causal: N > 4096), where they run the intra-wave
+ * on the 8-wave workgroups that d = 128 with N > 1024 (causal: N > 4096) and
+ * d = 64 with N > 2048 (causal: N > 8192) get, where they run the intra-wave
  * pipelined schedule of the FlashAttention-3 report, section 3.2: each wave
  * issues the matrix products of S(j+1) = Q K(j+1)^T and of O += P(j) V(j) one
  * at a time between the exponentials and sums of block j's softmax.  The two
