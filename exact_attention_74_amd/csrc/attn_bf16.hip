@@ -11,8 +11,8 @@
 // running sum l, one final normalisation).  Causal work at d <= 128 runs on
 // persistent workgroup slots over pairs of query blocks of equal total cost
 // (see the kernel below).  Head dim 256 runs 4-wave workgroups, one wave
-// per SIMD.  At head dims 64 and 128 the interior key tiles of the 8-wave
-// workgroups run software-pipelined (the next tile's S MFMAs issued
+// per SIMD.  At head dims 64 and 128 the interior key tiles run software-
+// pipelined (causal: on the 8-wave workgroups only) (the next tile's S MFMAs issued
 // between the current tile's exponentials, report section 3.2); every other
 // case runs the same-phase loop (both waves of a SIMD do MFMAs, then both do
 // softmax).
@@ -175,9 +175,10 @@ __device__ __forceinline__ void tile_compute(const char* smem, const uint32_t (&
 #undef TR_PAIR
 }
 
-// Software-pipelined interior tiles (head dims 64 and 128, 8-wave workgroups,
-// both masks: a causal block's tiles before its diagonal; the same-phase loop
-// below serves the edge tiles and every other case).  The FlashAttention-3
+// Software-pipelined interior tiles (head dims 64 and 128; non-causal on
+// both workgroup sizes, causal on the 8-wave workgroups, up to a block's
+// diagonal; the same-phase loop below serves the edge tiles and every other
+// case).  The FlashAttention-3
 // report (section 3.2) issues the next block's S = Q K^T before the current
 // block's softmax so that the matrix cores work while the exponentials run.
 // Here iteration j of a wave issues its MFMAs one per slot: the NS of
@@ -336,7 +337,7 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
                                            hh, scale_log2);                                     \
   } while (0)
   int kb = 0;
-  if constexpr (PIPE && D <= 128 && NW == 8) {
+  if constexpr (PIPE && D <= 128) {
     using P = fpipe::Slots<D>;
     // The pipelined loop over the interior tiles 0 .. nkb_int - 1 (an even
     // count, at least two; the edge tiles follow in the loops below).  LDS:
@@ -701,8 +702,11 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
     return launch_nw<D, CAUSAL, 4, false>(q, k, v, o, lse, B, H, Hkv, N, scale, stream);
   } else {
     const int small_n = (CAUSAL ? 4096 : 1024) * (128 / D);
+    // the pipelined loop on the 4-wave workgroups: non-causal only (+2-3% at
+    // N = 512-2048; causal, whose short blocks have few interior tiles, lost
+    // 3-5% at N = 512-1024)
     if (N <= small_n)
-      return launch_nw<D, CAUSAL, 4, false>(q, k, v, o, lse, B, H, Hkv, N, scale, stream);
+      return launch_nw<D, CAUSAL, 4, PIPE && !CAUSAL>(q, k, v, o, lse, B, H, Hkv, N, scale, stream);
     return launch_nw<D, CAUSAL, 8, PIPE>(q, k, v, o, lse, B, H, Hkv, N, scale, stream);
   }
 }
@@ -712,9 +716,10 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                                 int B, int H, int Hkv, int N, int d, bool causal,
                                 float softmax_scale, hipStream_t stream, bool same_phase) {
-  // d = 64 and 128 run the pipelined loop on their 8-wave workgroups (the
-  // same results as the same-phase loop, measured 1-4% faster, both masks);
-  // same_phase selects the same-phase loop there too, for comparison.
+  // d = 64 and 128 run the pipelined loop (the same results as the same-
+  // phase loop, measured 1-4% faster): on every workgroup size non-causal, on
+  // the 8-wave workgroups causal; same_phase selects the same-phase loop
+  // there too, for comparison.
   if (!same_phase && d == 128)
     return causal ? launch<128, true, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream)
                   : launch<128, false, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream);

@@ -77,7 +77,7 @@ extern "C" {
  *   softmax_scale  multiplies Q K^T; finite and > 0 (usually 1/sqrt(d)).
  * The score matrix is never materialised: each workgroup owns a block of
  * query rows of one (b, h) and streams K/V blocks through LDS; at d = 64 and
- * 128 on long sequences each wave software-pipelines the matrix products of
+ * 128 each wave software-pipelines the matrix products of
  * the next key block under the softmax of the current one (report section
  * 3.2; see attn_fwd_bf16_same_phase).
  */
@@ -87,12 +87,13 @@ int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* l
 /*
  * attn_fwd_bf16 with the same-phase schedule everywhere: both waves of a SIMD
  * issue a key tile's matrix products, then both run its softmax, one barrier
- * per tile.  attn_fwd_bf16 (and attn_fwd_bf16_gqa) use this schedule except
- * on the 8-wave workgroups that d = 128 with N > 1024 (causal: N > 4096) and
- * d = 64 with N > 2048 (causal: N > 8192) get, where they run the intra-wave
- * pipelined schedule of the FlashAttention-3 report, section 3.2: each wave
- * issues the matrix products of S(j+1) = Q K(j+1)^T and of O += P(j) V(j) one
- * at a time between the exponentials and sums of block j's softmax.  The two
+ * per tile.  attn_fwd_bf16 (and attn_fwd_bf16_gqa) use this schedule at
+ * d = 256, and causal with N <= 4096 (d = 128) or N <= 8192 (d = 64); in
+ * every other case they run the intra-wave pipelined schedule of the
+ * FlashAttention-3 report, section 3.2, over a block's interior key tiles:
+ * each wave issues the matrix products of S(j+1) = Q K(j+1)^T and of
+ * O += P(j) V(j) one at a time between the exponentials and sums of block j's
+ * softmax (the last, ragged or diagonal tiles run the same-phase loop).  The two
  * schedules compute every output element with the same operations in the
  * same order, so the results are identical bit for bit; this entry point
  * exists to compare them (the bench line's schedule leg).  Arguments,

@@ -272,13 +272,15 @@ def _default_vs_same_phase(dev, causal, scale):
     return to_np(o), lse.cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("N,d", [(1025, 128), (1088, 128), (1100, 128), (1500, 128), (2048, 128),
-                                 (2049, 64), (2112, 64), (2500, 64)])
+@pytest.mark.parametrize("N,d", [(128, 128), (129, 64), (640, 64), (1000, 128), (1025, 128),
+                                 (1088, 128), (1100, 128), (1500, 128), (2048, 128), (2049, 64),
+                                 (2112, 64), (2500, 64)])
 def test_pipelined_full_parity(N, d):
     """The pipelined loop (S(j+1) MFMAs between the exponentials of tile j),
-    which attn_fwd_bf16 runs on the 8-wave workgroups at d = 128 (N > 1024) and
-    d = 64 (N > 2048): every element against the oracle, and the outputs
-    bit-identical to the same-phase schedule's.  N = 1088 and 2112 leave an odd
+    which attn_fwd_bf16 runs non-causal at d = 64 and 128 on 4-wave (short N)
+    and 8-wave workgroups: every element against the oracle, and the outputs
+    bit-identical to the same-phase schedule's.  N = 128 is the shortest
+    pipelined run (one pair of tiles); N = 640, 1088 and 2112 leave an odd
     whole tile after the pipelined pairs, the others a ragged tail of 1 to 63
     keys."""
     w = workloads.Workload(f"pipe_n{N}_d{d}", 1, 3, N, d, False, seed=41 + N)
