@@ -222,6 +222,27 @@ struct Slots {
   static_assert(exps_in_time(), "an exponential after its P^T operand's first MFMA");
   static constexpr int kMax0 = N - 8;  // S(j+1)'s row max: slots kMax0 .. N - 1
 };
+// LDS slots of the pipelined loop.  R = 2: the two stages of the same-phase
+// loop ([K0 V0][K1 V1]); the next tile's copies can start only after the
+// barrier that frees their slots.  R = 4: [K0 K1 K2 K3][V0 V1 V2 V3] (8
+// tiles: 128 KB at d = 128, 64 KB at d = 64); the copies of K(j+3) and V(j+2) go out at the end of
+// iteration j, into slots freed two iterations earlier, so their issue (a
+// queue of 1 KB copies behind the other waves') overlaps the wait at the
+// next barrier instead of following it.  The V^T read addresses carry the V
+// region's base (VB), so every immediate offset stays below 64 KB.
+template <int D, int R>
+struct Ring {
+  using G = Geo<D>;
+  static constexpr int k(int i) { return R == 2 ? G::koff(i) : i * G::TILE; }
+  static constexpr int v(int i) { return R == 2 ? G::voff(i) : i * G::TILE; }
+  static constexpr int VB = R == 2 ? 0 : 4 * G::TILE;
+  static constexpr int kBytes = R == 2 ? 2 * G::STAGE : 8 * G::TILE;
+};
+// Ring size: 4 on the 8-wave workgroups (one per CU: their registers leave
+// room for no second one); 2 on the 4-wave ones, which share a CU with others
+// and would lose occupancy to the larger ring (-4.6% at B16 N1024 d64).
+template <int D, int NW>
+constexpr int ring() { return NW == 8 ? 4 : 2; }
 }  // namespace fpipe
 
 // One workgroup's work item: query block qblk (32 * NW rows) of head bh,
@@ -339,32 +360,47 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
   int kb = 0;
   if constexpr (PIPE && D <= 128) {
     using P = fpipe::Slots<D>;
+    constexpr int R = fpipe::ring<D, NW>();
+    using RG = fpipe::Ring<D, R>;
     // The pipelined loop over the interior tiles 0 .. nkb_int - 1 (an even
-    // count, at least two; the edge tiles follow in the loops below).  LDS:
-    // K(j) sits in K slot j % 2 and V(j) in V slot j % 2 of the two stages,
-    // but K is loaded one tile ahead: iteration j reads K(j+1) and V(j) and
-    // starts the copies of K(j+2) and V(j+1) into the slots that K(j) and
-    // V(j-1) left free.  Its barrier certifies that K(j+1) and V(j) have
-    // landed and that every wave is done with those two slots.
+    // count, at least two; the edge tiles follow in the loops below).  K(j)
+    // sits in K slot j % R and V(j) in V slot j % R, K loaded one tile ahead:
+    // iteration j reads K(j+1) and V(j).  R = 2: it starts the copies of
+    // K(j+2) and V(j+1) after its barrier, which certifies that K(j+1) and
+    // V(j) have landed and that every wave is done with the slots of K(j) and
+    // V(j-1).  R = 4: it ends by starting the copies of K(j+3) and V(j+2) (of
+    // tile nint - 1 again where those are past the interior, so that every
+    // iteration has the same copies in flight), and its barrier, fence-free,
+    // follows a wait that leaves the last iteration's copies in flight.
     if (nkb_int >= 2) {
       const int nint = nkb_int;
       auto load_k = [&](int slot, int k0) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t r = tile_rsrc(kh, (uint32_t)k0 * row_bytes, nbytes);
 #pragma unroll
         for (int i = 0; i < LOADS; ++i)
-          copy_to_lds16(r, smem + (wave * LOADS + i) * 1024 + G::koff(slot), voff_k[i]);
+          copy_to_lds16(r, smem + (wave * LOADS + i) * 1024 + RG::k(slot), voff_k[i]);
       };
       auto load_v = [&](int slot, int k0) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t r = tile_rsrc(vh, (uint32_t)k0 * row_bytes, nbytes);
 #pragma unroll
         for (int i = 0; i < LOADS; ++i)
-          copy_to_lds16(r, smem + (wave * LOADS + i) * 1024 + G::VBASE + G::voff(slot), voff_v[i]);
+          copy_to_lds16(r, smem + (wave * LOADS + i) * 1024 + RG::VB + RG::v(slot), voff_v[i]);
       };
       load_k(0, 0);
       load_v(0, 0);
       load_k(1, kBC);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
+      if constexpr (R == 4) {
+        load_k(2, (nint > 2 ? 2 : nint - 1) * kBC);
+        load_v(1, kBC);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * LOADS) : "memory");  // K(0) landed
+        __builtin_amdgcn_s_barrier();
+        // the V^T read addresses point into the V region for the loop
+#pragma unroll
+        for (int e = 0; e < D / 32; ++e) vaddr[e] += RG::VB;
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+      }
       // S(0) ahead of the loop, as in the same-phase tile body.
       f32x16 sA[2], sB[2];
       {
@@ -372,7 +408,7 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
         bf16x8 kf[NK];
         auto rd = [&](auto I) __attribute__((always_inline)) {
           constexpr int i = decltype(I)::value, t = i / 2, j = i % 2;
-          kf[i] = read_b128<G::koff(0) + j * 32 * G::RB>(kaddr[t]);
+          kf[i] = read_b128<RG::k(0) + j * 32 * G::RB>(kaddr[t]);
         };
         static_for<AHEAD>(rd);
         static_for<NK>([&](auto I) __attribute__((always_inline)) {
@@ -403,10 +439,16 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
       auto iter = [&](auto SK_, auto SV_, f32x16 (&cur)[2], f32x16 (&nxt)[2], int j)
                       __attribute__((always_inline)) {
         constexpr int SK = decltype(SK_)::value, SV = decltype(SV_)::value;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (j + 2 < nint) load_k(SV, (j + 2) * kBC);
-        if (j + 1 < nint) load_v(SK, (j + 1) * kBC);
+        if constexpr (R == 4) {
+          // K(j+1) and V(j) landed, K(j+2) and V(j+1) may still be in flight
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LOADS) : "memory");
+          __builtin_amdgcn_s_barrier();
+        } else {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
+          if (j + 2 < nint) load_k(SV, (j + 2) * kBC);
+          if (j + 1 < nint) load_v(SK, (j + 1) * kBC);
+        }
         raise_offset(mx);
         const float neg_m = -m;
         float rsum = 0.f;
@@ -420,11 +462,11 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
         auto issue = [&](auto R_) __attribute__((always_inline)) {
           constexpr int r = decltype(R_)::value;
           if constexpr (r < P::NS) {
-            kf[r] = read_b128<G::koff(SK) + (r % 2) * 32 * G::RB>(kaddr[r / 2]);
+            kf[r] = read_b128<RG::k(SK) + (r % 2) * 32 * G::RB>(kaddr[r / 2]);
           } else {
             constexpr int k = (r - P::NS) / 2, half = (r - P::NS) % 2, t2 = k / P::NE,
                           e = k % P::NE;
-            const bf16x4 x = read_tr16<G::voff(SV) + (16 * t2 + 8 * half) * G::RB>(vaddr[e]);
+            const bf16x4 x = read_tr16<RG::v(SV) + (16 * t2 + 8 * half) * G::RB>(vaddr[e]);
             if constexpr (half) vhi[k] = x; else vlo[k] = x;
           }
         };
@@ -486,23 +528,46 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
         });
         l += rsum;
         mx = max_halves(fmaxf(ma, mbx));
+        if constexpr (R == 4) {
+          load_k((SK + 2) % 4, min(j + 3, nint - 1) * kBC);
+          load_v((SV + 2) % 4, min(j + 2, nint - 1) * kBC);
+        }
       };
-      for (int j = 0; j + 2 < nint - 1; j += 2) {
+      if constexpr (R == 4) {
+        // nint - 1 iterations (an odd count), four per trip; iteration j has
+        // K slot (j+1) % 4, V slot j % 4, S(j) in sA for even j
+        int j = 0;
+        for (; j + 4 <= nint - 1; j += 4) {
+          iter(IC<1>{}, IC<0>{}, sA, sB, j);
+          iter(IC<2>{}, IC<1>{}, sB, sA, j + 1);
+          iter(IC<3>{}, IC<2>{}, sA, sB, j + 2);
+          iter(IC<0>{}, IC<3>{}, sB, sA, j + 3);
+        }
         iter(IC<1>{}, IC<0>{}, sA, sB, j);
-        iter(IC<0>{}, IC<1>{}, sB, sA, j + 1);
+        if (j + 1 < nint - 1) {
+          iter(IC<2>{}, IC<1>{}, sB, sA, j + 1);
+          iter(IC<3>{}, IC<2>{}, sA, sB, j + 2);
+        }
+      } else {
+        for (int j = 0; j + 2 < nint - 1; j += 2) {
+          iter(IC<1>{}, IC<0>{}, sA, sB, j);
+          iter(IC<0>{}, IC<1>{}, sB, sA, j + 1);
+        }
+        iter(IC<1>{}, IC<0>{}, sA, sB, nint - 2);
       }
-      iter(IC<1>{}, IC<0>{}, sA, sB, nint - 2);
-      // The last interior tile's P.V: V(nint-1) in V slot 1, S(nint-1) in sB.
+      // The last interior tile's P.V: V(nint-1) in V slot (nint-1) % R,
+      // S(nint-1) in sB.
       {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+        const uint32_t vs = (uint32_t)RG::v((nint - 1) % R);
         bf16x8 vf[4][P::NE];
 #pragma unroll
         for (int e = 0; e < P::NE; ++e)
 #pragma unroll
           for (int t2 = 0; t2 < 4; ++t2) {
-            const bf16x4 lo = read_tr16<0>(vaddr[e] + G::voff(1) + 16 * t2 * G::RB);
-            const bf16x4 hi = read_tr16<0>(vaddr[e] + G::voff(1) + (16 * t2 + 8) * G::RB);
+            const bf16x4 lo = read_tr16<0>(vaddr[e] + vs + 16 * t2 * G::RB);
+            const bf16x4 hi = read_tr16<0>(vaddr[e] + vs + (16 * t2 + 8) * G::RB);
             vf[t2][e] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           }
         raise_offset(mx);
@@ -526,7 +591,11 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
           for (int e = 0; e < P::NE; ++e) oacc[e] = mfma_bf16(vf[t2][e], pb[t2], oacc[e]);
       }
       kb = nint;
-      __syncthreads();  // every wave is done with both stages
+      if constexpr (R == 4) {
+#pragma unroll
+        for (int e = 0; e < D / 32; ++e) vaddr[e] -= RG::VB;
+      }
+      __syncthreads();  // every wave is done with the loop's slots
     }
   }
   if (kb < nkb) LOAD_TILE(0, kb * kBC);
@@ -592,7 +661,9 @@ __global__ __launch_bounds__(64 * NW, D > 128 ? 1 : 2) void attn_fwd_bf16_kernel
     __bf16* __restrict__ O, float* __restrict__ LSE, int H, int Hkv, int N, float scale_log2,
     int nqb, int xcd_remap, int nunits) {
   using G = Geo<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * G::STAGE];
+  constexpr int kSmem = PIPE && D <= 128 ? fpipe::Ring<D, fpipe::ring<D, NW>()>::kBytes : 2 * G::STAGE;
+  static_assert(kSmem >= 2 * G::STAGE, "the same-phase stages fit");
+  __shared__ __attribute__((aligned(1024))) char smem[kSmem];
   if constexpr (!persistent<D, CAUSAL>()) {
     const int L = blockIdx.x;
     int bh, qb;
