@@ -178,22 +178,22 @@ __device__ __forceinline__ void tile_compute(const char* smem, const uint32_t (&
 // Software-pipelined interior tiles (head dims 64 and 128; non-causal on
 // both workgroup sizes, causal on the 8-wave workgroups, up to a block's
 // diagonal; the same-phase loop below serves the edge tiles and every other
-// case).  The FlashAttention-3
-// report (section 3.2) issues the next block's S = Q K^T before the current
-// block's softmax so that the matrix cores work while the exponentials run.
-// Here iteration j of a wave issues its MFMAs one per slot: the NS of
-// S(j+1) = K(j+1) Q^T, then the NP of O^T += V(j)^T P(j)^T (d = 128: 16 + 16
-// slots, d = 64: 8 + 8).  Between them run the VALU work of tile j's softmax
-// and S(j+1)'s row max (the last 8 slots): exponential v (with its multiply-
-// add and row-sum add) in slot exp_slot(v), spread evenly over the slots
-// before the last P^T operand's first MFMA (d = 128: about one per slot), and
-// each bf16 pair packed in the slot of its second exponential, so every P^T
-// operand is complete before its first MFMA (d = 128: measured 0.8% faster
-// than two exponentials in each of 16 slots).  Each MFMA's K or V^T fragment
-// is read kLook reads ahead and waited for with an exact lgkmcnt count.  K is
-// loaded one tile ahead of V in the same two LDS stages (no extra LDS).  Every
-// output element goes through the same operations in the same order as in the
-// same-phase loop, so the results are bit-identical to it.
+// case).  The FlashAttention-3 report (section 3.2) issues the next block's
+// S = Q K^T before the current block's softmax so that the matrix cores work
+// while the exponentials run.  Here iteration j of a wave issues its MFMAs one
+// per slot: the NS of S(j+1) = K(j+1) Q^T, then the NP of
+// O^T += V(j)^T P(j)^T (d = 128: 16 + 16 slots, d = 64: 8 + 8).  Between them
+// run the VALU work of tile j's softmax and S(j+1)'s row max (the last 8
+// slots): exponential v (with its multiply-add and row-sum add) in slot
+// exp_slot(v), spread evenly over the slots before the last P^T operand's
+// first MFMA (d = 128: about one per slot), and each bf16 pair packed in the
+// slot of its second exponential, so every P^T operand is complete before its
+// first MFMA (d = 128: measured 0.8% faster than two exponentials in each of
+// 16 slots).  Each MFMA's K or V^T fragment is read kLook reads ahead and
+// waited for with an exact lgkmcnt count.  K is loaded one tile ahead of V in
+// an LDS ring of R slots each (Ring below).  Every output element goes through
+// the same operations in the same order as in the same-phase loop, so the
+// results are bit-identical to it.
 namespace fpipe {
 constexpr int kLook = 5;  // LDS reads in flight ahead of the MFMA that needs them
 template <int D>
@@ -225,10 +225,10 @@ struct Slots {
 // LDS slots of the pipelined loop.  R = 2: the two stages of the same-phase
 // loop ([K0 V0][K1 V1]); the next tile's copies can start only after the
 // barrier that frees their slots.  R = 4: [K0 K1 K2 K3][V0 V1 V2 V3] (8
-// tiles: 128 KB at d = 128, 64 KB at d = 64); the copies of K(j+3) and V(j+2) go out at the end of
-// iteration j, into slots freed two iterations earlier, so their issue (a
-// queue of 1 KB copies behind the other waves') overlaps the wait at the
-// next barrier instead of following it.  The V^T read addresses carry the V
+// tiles: 128 KB at d = 128, 64 KB at d = 64); the copies of K(j+3) and V(j+2)
+// go out at the end of iteration j, into slots freed two iterations earlier,
+// so their issue (a queue of 1 KB copies behind the other waves') overlaps
+// the wait at the next barrier instead of following it.  The V^T read addresses carry the V
 // region's base (VB), so every immediate offset stays below 64 KB.
 template <int D, int R>
 struct Ring {
