@@ -36,12 +36,14 @@ def hipcc() -> str:
 # Per-source extra flags.  -fno-honor-nans lets max() of MFMA results lower to
 # v_max3_f32 without NaN-quieting copies (the attention kernels never form a
 # NaN from valid input; infinities, used for masking, are still honoured).
-# -amdgpu-mfma-vgpr-form: the gradient kernels' compiler-issued MFMAs write
-# VGPRs (S and dP are read by the VALU right away); the dK/dV accumulators
-# that need the AGPR file at head dim 128 are placed there by the kernel's
-# own assembly MFMAs, so no accumulator is copied between the two files.
+# -amdgpu-mfma-vgpr-form: the compiler-issued MFMAs write VGPRs (S and dP are
+# read by the VALU right away); the accumulators that need the AGPR file (the
+# gradients' dK/dV at head dim 128, the bf16 forward's O at head dim 256) are
+# placed there by the kernels' own assembly MFMAs, so no accumulator is copied
+# between the two files.  (At head dims 64 and 128 the forward kernels fit
+# the 256 VGPRs, and the flag leaves their code unchanged.)
 EXTRA = {
-    "attn_bf16.hip": ["-fno-honor-nans"],
+    "attn_bf16.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
     "attn_fp8.hip": ["-fno-honor-nans"],
     "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }

@@ -11,11 +11,11 @@
 // running sum l, one final normalisation).  Causal work at d <= 128 runs on
 // persistent workgroup slots over pairs of query blocks of equal total cost
 // (see the kernel below).  Head dim 256 runs 4-wave workgroups, one wave
-// per SIMD.  At head dims 64 and 128 the interior key tiles run software-
-// pipelined (causal: on the 8-wave workgroups only) (the next tile's S MFMAs issued
-// between the current tile's exponentials, report section 3.2); every other
-// case runs the same-phase loop (both waves of a SIMD do MFMAs, then both do
-// softmax).
+// per SIMD, with O in the AGPR file.  The interior key tiles run software-
+// pipelined (the next tile's S MFMAs issued between the current tile's
+// exponentials, report section 3.2): non-causal at every head dim, causal on
+// the 8-wave workgroups (d = 64 and 128); every other case runs the
+// same-phase loop (both waves of a SIMD do MFMAs, then both do softmax).
 //
 // Transposed formulation.  Each wave computes S^T = K Q^T (keys as MFMA rows,
 // its 32 queries as MFMA columns), so the accumulator keeps every query on one
@@ -81,6 +81,44 @@ __device__ __forceinline__ float rowmax(const f32x16 (&s)[2]) {
   return fmaxf(a, b);
 }
 
+// Head dim 256: O^T (128 registers a lane) stays in the AGPR file from its
+// zeroing to the epilogue.  Its P.V products are assembly MFMAs on "+a"
+// operands (the compiler's own MFMAs write VGPRs, -amdgpu-mfma-vgpr-form), so
+// that Q^T, S and the softmax keep the 256 VGPRs and O is never copied
+// between the two files in the tile loops.  The compiler does not see the
+// MFMAs inside the assembly, so the wait states around them are explicit: a
+// leading s_nop 1 for a B operand just written by the VALU, and o_fence (24
+// wait states) between the accumulators' MFMAs and any other instruction
+// that touches them (the rescale, the epilogue).
+template <bool NOP2>
+__device__ __forceinline__ void mfma_o(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  if constexpr (NOP2)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+template <int D>
+__device__ __forceinline__ void o_fence(f32x16 (&o)[D / 32]) {
+  if constexpr (D > 128)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]),
+                   "+a"(o[6]), "+a"(o[7]));
+}
+// O^T[e] += a b; NOP2: b may have been written by the VALU just before.
+template <int D, bool NOP2>
+__device__ __forceinline__ void pv_mfma(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  if constexpr (D > 128) mfma_o<NOP2>(acc, a, b);
+  else acc = mfma_bf16(a, b, acc);
+}
+// O^T *= alpha (the rare lazy-offset raise; at d = 256 through the AGPRs).
+template <int D>
+__device__ __forceinline__ void o_scale(f32x16 (&o)[D / 32], float alpha) {
+  o_fence<D>(o);
+#pragma unroll
+  for (int e = 0; e < D / 32; ++e) o[e] *= alpha;
+  o_fence<D>(o);
+}
+
 // One key tile in LDS stage ST: S^T = K Q^T, (masking,) online softmax with
 // lazy offset, and O^T += V^T P^T.  smem: the LDS tile buffers; vaddr: LDS
 // addresses of this lane's V^T fragment sources in stage 0's V buffer.
@@ -138,8 +176,7 @@ __device__ __forceinline__ void tile_compute(const char* smem, const uint32_t (&
     const float alpha = exp2_fast(m - m_new);
     m = m_new;
     l *= alpha;
-#pragma unroll
-    for (int e = 0; e < D / 32; ++e) oacc[e] *= alpha;
+    o_scale<D>(oacc, alpha);
   }
   const float neg_m = -m;
   float rsum = 0.f;
@@ -156,10 +193,13 @@ __device__ __forceinline__ void tile_compute(const char* smem, const uint32_t (&
 
   // O^T += V^T P^T.
   lds_wait_v(vf);
-#pragma unroll
-  for (int t2 = 0; t2 < 4; ++t2)
-#pragma unroll
-    for (int e = 0; e < NEH; ++e) oacc[e] = mfma_bf16(vf[t2][e], pb[t2], oacc[e]);
+  static_for<4>([&](auto T2) __attribute__((always_inline)) {
+    constexpr int t2 = decltype(T2)::value;
+    static_for<NEH>([&](auto E) __attribute__((always_inline)) {
+      constexpr int e = decltype(E)::value;
+      pv_mfma<D, e == 0>(oacc[e], vf[t2][e], pb[t2]);
+    });
+  });
   if constexpr (NHALF == 2) {
 #pragma unroll
     for (int e = 0; e < NEH; ++e) {
@@ -167,22 +207,26 @@ __device__ __forceinline__ void tile_compute(const char* smem, const uint32_t (&
       TR_PAIR(2, e, vaddr[NEH + e]) TR_PAIR(3, e, vaddr[NEH + e])
     }
     lds_wait_v(vf);
-#pragma unroll
-    for (int t2 = 0; t2 < 4; ++t2)
-#pragma unroll
-      for (int e = 0; e < NEH; ++e) oacc[NEH + e] = mfma_bf16(vf[t2][e], pb[t2], oacc[NEH + e]);
+    static_for<4>([&](auto T2) __attribute__((always_inline)) {
+      constexpr int t2 = decltype(T2)::value;
+      static_for<NEH>([&](auto E) __attribute__((always_inline)) {
+        constexpr int e = decltype(E)::value;
+        pv_mfma<D, e == 0>(oacc[NEH + e], vf[t2][e], pb[t2]);
+      });
+    });
   }
 #undef TR_PAIR
 }
 
-// Software-pipelined interior tiles (head dims 64 and 128; non-causal on
-// both workgroup sizes, causal on the 8-wave workgroups, up to a block's
+// Software-pipelined interior tiles (non-causal at every head dim and on
+// both workgroup sizes; causal on the 8-wave workgroups, up to a block's
 // diagonal; the same-phase loop below serves the edge tiles and every other
 // case).  The FlashAttention-3 report (section 3.2) issues the next block's
 // S = Q K^T before the current block's softmax so that the matrix cores work
 // while the exponentials run.  Here iteration j of a wave issues its MFMAs one
 // per slot: the NS of S(j+1) = K(j+1) Q^T, then the NP of
-// O^T += V(j)^T P(j)^T (d = 128: 16 + 16 slots, d = 64: 8 + 8).  Between them
+// O^T += V(j)^T P(j)^T (d = 256: 32 + 32 slots, d = 128: 16 + 16, d = 64:
+// 8 + 8).  Between them
 // run the VALU work of tile j's softmax and S(j+1)'s row max (the last 8
 // slots): exponential v (with its multiply-add and row-sum add) in slot
 // exp_slot(v), spread evenly over the slots before the last P^T operand's
@@ -338,6 +382,7 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int e = 0; e < D / 32; ++e) oacc[e] = f32x16{};
+  o_fence<D>(oacc);
 
   const int nkb_all = ceil_div(N, kBC);
   const int nkb = CAUSAL ? min(nkb_all, ceil_div(min(N, (qblk + 1) * kBR), kBC)) : nkb_all;
@@ -358,7 +403,7 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
                                            hh, scale_log2);                                     \
   } while (0)
   int kb = 0;
-  if constexpr (PIPE && D <= 128) {
+  if constexpr (PIPE) {
     using P = fpipe::Slots<D>;
     constexpr int R = fpipe::ring<D, NW>();
     using RG = fpipe::Ring<D, R>;
@@ -384,7 +429,8 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
         const __amdgpu_buffer_rsrc_t r = tile_rsrc(vh, (uint32_t)k0 * row_bytes, nbytes);
 #pragma unroll
         for (int i = 0; i < LOADS; ++i)
-          copy_to_lds16(r, smem + (wave * LOADS + i) * 1024 + RG::VB + RG::v(slot), voff_v[i]);
+          copy_to_lds16(r, smem + (wave * LOADS + i) * 1024 + (R == 2 ? G::VBASE : RG::VB) + RG::v(slot),
+                        voff_v[i]);
       };
       load_k(0, 0);
       load_v(0, 0);
@@ -430,8 +476,7 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
           const float alpha = exp2_fast(m - m_new);
           m = m_new;
           l *= alpha;
-#pragma unroll
-          for (int e = 0; e < D / 32; ++e) oacc[e] *= alpha;
+          o_scale<D>(oacc, alpha);
         }
       };
       // Iteration j: K slot SK holds K(j+1), V slot SV holds V(j); cur = S(j),
@@ -491,7 +536,7 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
             const bf16x8 pb = __builtin_bit_cast(
                 bf16x8, i32x4{(int)pw[4 * t2], (int)pw[4 * t2 + 1], (int)pw[4 * t2 + 2],
                               (int)pw[4 * t2 + 3]});
-            oacc[e] = mfma_bf16(vf, pb, oacc[e]);
+            pv_mfma<D, e == 0>(oacc[e], vf, pb);
           }
           constexpr int first = P::issued(s - 1) + 1;
           static_for<P::issued(s) - P::issued(s - 1)>([&](auto K_) __attribute__((always_inline)) {
@@ -561,15 +606,21 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         const uint32_t vs = (uint32_t)RG::v((nint - 1) % R);
-        bf16x8 vf[4][P::NE];
+        // V^T operands in halves of at most four 32-dim blocks (d = 256: two)
+        constexpr int NEH = P::NE <= 4 ? P::NE : 4;
+        bf16x8 vf[4][NEH];
+        auto read_half = [&](auto HF) __attribute__((always_inline)) {
+          constexpr int hf = decltype(HF)::value;
 #pragma unroll
-        for (int e = 0; e < P::NE; ++e)
+          for (int e = 0; e < NEH; ++e)
 #pragma unroll
-          for (int t2 = 0; t2 < 4; ++t2) {
-            const bf16x4 lo = read_tr16<0>(vaddr[e] + vs + 16 * t2 * G::RB);
-            const bf16x4 hi = read_tr16<0>(vaddr[e] + vs + (16 * t2 + 8) * G::RB);
-            vf[t2][e] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          }
+            for (int t2 = 0; t2 < 4; ++t2) {
+              const bf16x4 lo = read_tr16<0>(vaddr[hf * NEH + e] + vs + 16 * t2 * G::RB);
+              const bf16x4 hi = read_tr16<0>(vaddr[hf * NEH + e] + vs + (16 * t2 + 8) * G::RB);
+              vf[t2][e] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+        };
+        read_half(IC<0>{});
         raise_offset(mx);
         const float neg_m = -m;
         float rsum = 0.f;
@@ -584,11 +635,18 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
             pb[t2][sl] = (__bf16)pv;
           }
         l += rsum;
-        lds_wait_v(vf);
-#pragma unroll
-        for (int t2 = 0; t2 < 4; ++t2)
-#pragma unroll
-          for (int e = 0; e < P::NE; ++e) oacc[e] = mfma_bf16(vf[t2][e], pb[t2], oacc[e]);
+        static_for<P::NE / NEH>([&](auto HF) __attribute__((always_inline)) {
+          constexpr int hf = decltype(HF)::value;
+          if constexpr (hf > 0) read_half(HF);
+          lds_wait_v(vf);
+          static_for<4>([&](auto T2) __attribute__((always_inline)) {
+            constexpr int t2 = decltype(T2)::value;
+            static_for<NEH>([&](auto E) __attribute__((always_inline)) {
+              constexpr int e = decltype(E)::value;
+              pv_mfma<D, e == 0>(oacc[hf * NEH + e], vf[t2][e], pb[t2]);
+            });
+          });
+        });
       }
       kb = nint;
       if constexpr (R == 4) {
@@ -617,6 +675,7 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
   // except causal d = 256 (1% slower), which stores directly.
   const float lt = sum_halves(l);
   const float inv = 1.f / lt;
+  o_fence<D>(oacc);
   if constexpr (!(CAUSAL && D > 128)) {
     __syncthreads();
     store_rows_via_lds<D>(smem + wave * 32 * (2 * D), oacc, inv, O, head_off, rs, q0, N, lane);
@@ -661,7 +720,7 @@ __global__ __launch_bounds__(64 * NW, D > 128 ? 1 : 2) void attn_fwd_bf16_kernel
     __bf16* __restrict__ O, float* __restrict__ LSE, int H, int Hkv, int N, float scale_log2,
     int nqb, int xcd_remap, int nunits) {
   using G = Geo<D>;
-  constexpr int kSmem = PIPE && D <= 128 ? fpipe::Ring<D, fpipe::ring<D, NW>()>::kBytes : 2 * G::STAGE;
+  constexpr int kSmem = PIPE ? fpipe::Ring<D, fpipe::ring<D, NW>()>::kBytes : 2 * G::STAGE;
   static_assert(kSmem >= 2 * G::STAGE, "the same-phase stages fit");
   __shared__ __attribute__((aligned(1024))) char smem[kSmem];
   if constexpr (!persistent<D, CAUSAL>()) {
@@ -768,9 +827,10 @@ template <int D, bool CAUSAL, bool PIPE = false>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                   int Hkv, int N, float scale, hipStream_t stream) {
   // d = 256: one wave per SIMD (Q fragments and O take 192 registers), so
-  // always four waves.
+  // always four waves; the pipelined loop non-causal (+11.6% at B2 H16
+  // N8192), the same-phase loop causal.
   if constexpr (D > 128) {
-    return launch_nw<D, CAUSAL, 4, false>(q, k, v, o, lse, B, H, Hkv, N, scale, stream);
+    return launch_nw<D, CAUSAL, 4, PIPE && !CAUSAL>(q, k, v, o, lse, B, H, Hkv, N, scale, stream);
   } else {
     const int small_n = (CAUSAL ? 4096 : 1024) * (128 / D);
     // the pipelined loop on the 4-wave workgroups: non-causal only (+2-3% at
@@ -787,16 +847,18 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                                 int B, int H, int Hkv, int N, int d, bool causal,
                                 float softmax_scale, hipStream_t stream, bool same_phase) {
-  // d = 64 and 128 run the pipelined loop (the same results as the same-
-  // phase loop, measured 1-4% faster): on every workgroup size non-causal, on
-  // the 8-wave workgroups causal; same_phase selects the same-phase loop
-  // there too, for comparison.
+  // The pipelined loop (the same results as the same-phase loop, measured
+  // 1-4% faster at d = 64 and 128, 12% at d = 256): non-causal at every head
+  // dim and workgroup size, causal on the 8-wave workgroups (d = 64 and 128);
+  // same_phase selects the same-phase loop there too, for comparison.
   if (!same_phase && d == 128)
     return causal ? launch<128, true, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream)
                   : launch<128, false, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream);
   if (!same_phase && d == 64)
     return causal ? launch<64, true, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream)
                   : launch<64, false, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream);
+  if (!same_phase && d == 256 && !causal)
+    return launch<256, false, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream);
   if (d == 256)
     return causal ? launch<256, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream)
                   : launch<256, false>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream);

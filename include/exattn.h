@@ -76,10 +76,10 @@ extern "C" {
  *   causal       0 or 1.
  *   softmax_scale  multiplies Q K^T; finite and > 0 (usually 1/sqrt(d)).
  * The score matrix is never materialised: each workgroup owns a block of
- * query rows of one (b, h) and streams K/V blocks through LDS; at d = 64 and
- * 128 each wave software-pipelines the matrix products of
- * the next key block under the softmax of the current one (report section
- * 3.2; see attn_fwd_bf16_same_phase).
+ * query rows of one (b, h) and streams K/V blocks through LDS; each wave
+ * software-pipelines the matrix products of the next key block under the
+ * softmax of the current one (report section 3.2; see
+ * attn_fwd_bf16_same_phase for where it does).
  */
 int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                   int B, int H, int N, int d, int causal, float softmax_scale, void* stream);
@@ -87,8 +87,8 @@ int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* l
 /*
  * attn_fwd_bf16 with the same-phase schedule everywhere: both waves of a SIMD
  * issue a key tile's matrix products, then both run its softmax, one barrier
- * per tile.  attn_fwd_bf16 (and attn_fwd_bf16_gqa) use this schedule at
- * d = 256, and causal with N <= 4096 (d = 128) or N <= 8192 (d = 64); in
+ * per tile.  attn_fwd_bf16 (and attn_fwd_bf16_gqa) use this schedule causal
+ * at d = 256, and causal with N <= 4096 (d = 128) or N <= 8192 (d = 64); in
  * every other case they run the intra-wave pipelined schedule of the
  * FlashAttention-3 report, section 3.2, over a block's interior key tiles:
  * each wave issues the matrix products of S(j+1) = Q K(j+1)^T and of

@@ -274,15 +274,16 @@ def _default_vs_same_phase(dev, causal, scale):
 
 @pytest.mark.parametrize("N,d", [(128, 128), (129, 64), (640, 64), (1000, 128), (1025, 128),
                                  (1088, 128), (1100, 128), (1500, 128), (2048, 128), (2049, 64),
-                                 (2112, 64), (2500, 64)])
+                                 (2112, 64), (2500, 64), (128, 256), (191, 256), (640, 256),
+                                 (1000, 256)])
 def test_pipelined_full_parity(N, d):
     """The pipelined loop (S(j+1) MFMAs between the exponentials of tile j),
-    which attn_fwd_bf16 runs non-causal at d = 64 and 128 on 4-wave (short N)
-    and 8-wave workgroups: every element against the oracle, and the outputs
-    bit-identical to the same-phase schedule's.  N = 128 is the shortest
-    pipelined run (one pair of tiles); N = 640, 1088 and 2112 leave an odd
-    whole tile after the pipelined pairs, the others a ragged tail of 1 to 63
-    keys."""
+    which attn_fwd_bf16 runs non-causal on 4-wave (short N, and d = 256 with O
+    in the AGPR file) and 8-wave workgroups: every element against the oracle,
+    and the outputs bit-identical to the same-phase schedule's.  N = 128 is
+    the shortest pipelined run (one pair of tiles); N = 640, 1088 and 2112
+    leave an odd whole tile after the pipelined pairs, the others a ragged
+    tail of 1 to 63 keys."""
     w = workloads.Workload(f"pipe_n{N}_d{d}", 1, 3, N, d, False, seed=41 + N)
     say(w.name)
     host, dev = bf16_inputs(w)
@@ -296,13 +297,15 @@ def test_pipelined_full_parity(N, d):
                                             (1, 3, 5000, 128, True), (1, 2, 8300, 64, True),
                                             (1, 4, 1024, 128, False),
                                             (1, 3, 3000, 64, False), (1, 3, 3000, 128, True),
-                                            (1, 2, 700, 256, False), (2, 2, 1, 128, False)])
+                                            (1, 2, 700, 256, True), (2, 8, 8192, 256, False),
+                                            (2, 2, 1, 128, False)])
 def test_schedules_sampled_rows(B, H, N, d, causal):
-    """The bench shape B2 H16 N8192, d = 64 N = 3000 and causal N = 5000,
-    8192 (d = 128) and 8300 (d = 64) through the pipelined loop (sampled rows
-    against the oracle; causal blocks run it up to their diagonal), and the
-    shapes that run the same-phase loop under both entry points (short N,
-    causal d = 128 N <= 4096, d = 256, one token): bit-identical."""
+    """The bench shapes B2 H16 N8192 (d = 128) and B2 H8 N8192 (d = 256),
+    d = 64 N = 3000 and causal N = 5000, 8192 (d = 128) and 8300 (d = 64)
+    through the pipelined loop (sampled rows against the oracle; causal blocks
+    run it up to their diagonal), and the shapes that run the same-phase loop
+    under both entry points (short N, causal d = 128 N <= 4096, causal
+    d = 256, one token): bit-identical."""
     w = workloads.Workload(f"sched_b{B}h{H}n{N}d{d}", B, H, N, d, causal, seed=7 + N)
     say(w.name + ("_causal" if causal else ""))
     host, dev = bf16_inputs(w)
