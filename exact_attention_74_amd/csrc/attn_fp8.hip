@@ -138,6 +138,31 @@ __device__ __forceinline__ void read_vt(const uint32_t* vaddr, i32x8 (&vf)[2][NE
   }
 }
 
+// Head dim 256: the P.V products are assembly MFMAs on "+v" operands, so O
+// (rescaled by the VALU every tile) stays in VGPRs and the compiler's own
+// MFMAs (S) take the AGPRs.  The wait states the compiler cannot see are
+// explicit: a leading s_nop 1 where an operand was just written by the VALU,
+// and o8_fence (24 wait states) between O's MFMAs and the VALU's next use.
+template <bool NOP2>
+__device__ __forceinline__ void mfma8_v(f32x16& acc, const i32x8& a, const i32x8& b) {
+  if constexpr (NOP2)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+template <int D, bool NOP2>
+__device__ __forceinline__ void pv8(f32x16& acc, const i32x8& a, const i32x8& b) {
+  if constexpr (D > 128) mfma8_v<NOP2>(acc, a, b);
+  else acc = mfma_fp8(a, b, acc);
+}
+template <int D>
+__device__ __forceinline__ void o8_fence(f32x16 (&o)[D / 32]) {
+  if constexpr (D > 128)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]), "+v"(o[4]), "+v"(o[5]),
+                   "+v"(o[6]), "+v"(o[7]));
+}
+
 // Causal work runs persistent at d <= 128 (at d = 256 the loop around the
 // body would not fit the registers of the one-wave-per-SIMD kernel).
 template <int D, bool CAUSAL>
@@ -309,6 +334,7 @@ _Pragma("unroll")                                                               
     /* hardware reciprocal (1 ulp): the ratio only rescales the fp32 accumulator */                \
     const float f = alpha * (sv_prev * __builtin_amdgcn_rcpf(sv));                                   \
     sv_prev = sv;                                                                                    \
+    o8_fence<D>(oacc);                                                                               \
 _Pragma("unroll")                                                                                    \
     for (int e = 0; e < D / 32; ++e) oacc[e] *= f;                                                   \
                                                                                                      \
@@ -319,6 +345,7 @@ _Pragma("unroll")                                                               
       for (int u = 0; u < 2; ++u)                                                                    \
 _Pragma("unroll")                                                                                    \
         for (int e = 0; e < NEH; ++e) oacc[e] = mfma_fp8(vf0[u][e], pf[u], oacc[e]);                 \
+      static_assert(D <= 128, "early V^T reads at d <= 128 only");                                   \
     } else {                                                                                         \
       /* V^T operands in halves of at most four 32-dim blocks (d = 256: two) */                    \
 _Pragma("unroll")                                                                                    \
@@ -326,11 +353,13 @@ _Pragma("unroll")                                                               
         i32x8 vf[2][NEH];                                                                            \
         read_vt<D, ST, NEH>(vaddr + hf * NEH, vf);                                                   \
         lds_wait_v(vf);                                                                              \
-_Pragma("unroll")                                                                                    \
-        for (int u = 0; u < 2; ++u)                                                                  \
-_Pragma("unroll")                                                                                    \
-          for (int e = 0; e < NEH; ++e)                                                              \
-            oacc[hf * NEH + e] = mfma_fp8(vf[u][e], pf[u], oacc[hf * NEH + e]);                      \
+        static_for<2>([&](auto U_) {                                                                 \
+          constexpr int u = decltype(U_)::value;                                                     \
+          static_for<NEH>([&](auto E_) {                                                             \
+            constexpr int e = decltype(E_)::value;                                                   \
+            pv8<D, u == 0 || e == 0>(oacc[hf * NEH + e], vf[u][e], pf[u]);                           \
+          });                                                                                        \
+        });                                                                                          \
       }                                                                                              \
     }                                                                                                \
 
@@ -366,6 +395,7 @@ _Pragma("unroll")                                                               
   // store measured 3% slower in the persistent causal kernel).
   const float lt = sum_halves(l);
   const float inv = sv_prev / lt;
+  o8_fence<D>(oacc);
   if constexpr (!CAUSAL) {
     static_assert(G::NW * 32 * 2 * D <= 2 * G::STAGE, "the output rows are staged in the tile buffers");
     __syncthreads();

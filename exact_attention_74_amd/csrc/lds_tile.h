@@ -4,9 +4,6 @@
 // assembly with explicit wait counts.
 #pragma once
 
-#include <type_traits>
-#include <utility>
-
 #include "common.h"
 
 namespace exattn {
@@ -83,17 +80,6 @@ __device__ __forceinline__ bf16x8 read_b128(uint32_t addr) {
 template <int N>
 __device__ __forceinline__ void wait_lds(bf16x8& x) {
   asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "n"(N));
-}
-
-template <int V>
-using IC = std::integral_constant<int, V>;
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(IC<I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // Waits for every outstanding LDS read, passing the V^T fragments through so
