@@ -163,6 +163,66 @@ __device__ __forceinline__ void o8_fence(f32x16 (&o)[D / 32]) {
                    "+v"(o[6]), "+v"(o[7]));
 }
 
+
+// Software-pipelined interior tiles at head dim 256 (non-causal): one wave
+// per SIMD, so no second wave's MFMAs cover the softmax; instead iteration j
+// of a wave issues its MFMAs one per slot, the 16 of S(j+1) = K(j+1) Q^T and
+// then the 16 of O^T += V(j)^T P(j)^T, with tile j's softmax (the exponentials,
+// the O rescale) and S(j+1)'s row max spread between them (the FlashAttention-3
+// report, section 3.2: the next block's S = Q K^T before the current block's
+// softmax).  S(j+1) accumulates in AGPRs (assembly MFMAs, Q^T in AGPRs too),
+// read by the VALU one value at a time; O stays in VGPRs for the per-tile
+// rescale.  Each MFMA's operand is read kLook reads ahead and waited for with
+// an exact lgkmcnt count.  The next tiles' sixteen 1 KB copies per wave go
+// out one per slot in the first sixteen slots, under the MFMAs (issued
+// together after the barrier they stalled the wave for most of a tile's
+// softmax; one every two slots lands too late).  Every output element goes
+// through the operations of the same-phase tile body in the same order, so
+// the results are identical.
+namespace fpipe8 {
+constexpr int NS = 16;   // S(j+1) MFMAs: key block s % 4, k-step s / 4
+constexpr int NP = 16;   // P.V MFMAs: key half u = k / 8, 32-dim block e = k % 8
+constexpr int N = NS + NP;
+constexpr int kLook = 6;
+constexpr int kLast = 2 * NS + 4 * NP - 1;  // reads: 2 per S MFMA, 4 per P.V MFMA
+// last read slot s's MFMA needs
+constexpr int need(int s) { return s < NS ? 2 * s + 1 : 2 * NS + 4 * (s - NS) + 3; }
+// reads issued by the end of slot s (s = -1: the prologue)
+constexpr int issued(int s) {
+  return s < 0 ? kLook : (need(s) + kLook < kLast ? need(s) + kLook : kLast);
+}
+// exponential v (0 .. 63, in the same-phase body's order) in slot exp_slot(v):
+// P^T half u is complete before its first MFMA (slot NS + 8 u)
+constexpr int exp_slot(int v) { return (3 * v) / 8; }
+// O^T block e rescaled in slots 2e, 2e + 1 (before its first P.V MFMA)
+constexpr int kMax0 = 24;  // S(j+1)'s row max: slots 24 .. 31, eight values each
+}  // namespace fpipe8
+
+template <int OFF>
+__device__ __forceinline__ i32x4 read_k16(uint32_t addr) {
+  i32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+// S MFMA on an AGPR accumulator, Q^T from AGPRs; FIRST: the k-step that
+// starts the sum (accumulator input 0); NOP2: Q^T may just have been copied
+// into the AGPRs.
+template <bool FIRST, bool NOP2>
+__device__ __forceinline__ void mfma8_sa(f32x16& acc, const i32x8& k, const i32x8& q) {
+  if constexpr (FIRST && NOP2)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=a"(acc) : "v"(k), "a"(q));
+  else if constexpr (FIRST)
+    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=a"(acc) : "v"(k), "a"(q));
+  else if constexpr (NOP2)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(acc) : "v"(k), "a"(q));
+  else
+    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(acc) : "v"(k), "a"(q));
+}
+// Wait states between S's MFMAs and the VALU's reads of it.
+__device__ __forceinline__ void s_fence(f32x16 (&s)[4]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(s[0]), "+a"(s[1]), "+a"(s[2]), "+a"(s[3]));
+}
+
 // Causal work runs persistent at d <= 128 (at d = 256 the loop around the
 // body would not fit the registers of the one-wave-per-SIMD kernel).
 template <int D, bool CAUSAL>
@@ -375,8 +435,239 @@ _Pragma("unroll")                                                               
     }                                                                                                \
   } while (0)
   const int nkb_int = min(nkb, min(CAUSAL ? qblk * (kBR / kBC) : nkb, N / kBC)) & ~1;
-  LOAD_TILE(0, 0);
+
   int kb2 = 0;
+  if constexpr (D > 128 && !CAUSAL) {
+    if (nkb_int >= 2) {
+      namespace P8 = fpipe8;
+      const int nint = nkb_int;
+      const uint32_t lbase = lds_addr(smem);
+      uint32_t kad[D / 64][2];
+#pragma unroll
+      for (int t = 0; t < D / 64; ++t) {
+        kad[t][0] = lbase + (uint32_t)kaddr[t][0];
+        kad[t][1] = lbase + (uint32_t)kaddr[t][1];
+      }
+      auto load_k = [&](int slot, int k0) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t r = tile_rsrc(kh, (uint32_t)k0 * row_bytes, nbytes);
+#pragma unroll
+        for (int i = 0; i < G::LOADS; ++i)
+          copy_to_lds16(r, smem + (wave * G::LOADS + i) * 1024 + G::koff(slot), voff_k[i]);
+      };
+      auto load_v = [&](int slot, int k0) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t r = tile_rsrc(vh, (uint32_t)k0 * row_bytes, nbytes);
+#pragma unroll
+        for (int i = 0; i < G::LOADS; ++i)
+          copy_to_lds16(r, smem + (wave * G::LOADS + i) * 1024 + G::VBASE + G::voff(slot), voff_v[i]);
+      };
+      load_k(0, 0);
+      load_v(0, 0);
+      load_k(1, kBC);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      f32x16 sA[4], sB[4];
+      // S(0) = K(0) Q^T (K slot 0), then its row max
+      {
+        i32x4 klo[P8::NS], khi[P8::NS];
+        auto rd = [&](auto I) __attribute__((always_inline)) {
+          constexpr int i = decltype(I)::value, jb = i % 4, t = i / 4;
+          klo[i] = read_k16<G::koff(0) + jb * 32 * G::RB>(kad[t][0]);
+          khi[i] = read_k16<G::koff(0) + jb * 32 * G::RB>(kad[t][1]);
+        };
+        constexpr int AHEAD = 4;
+        static_for<AHEAD>(rd);
+        static_for<P8::NS>([&](auto I) __attribute__((always_inline)) {
+          constexpr int i = decltype(I)::value, jb = i % 4, t = i / 4;
+          constexpr int nis = (AHEAD + i < P8::NS) ? AHEAD + i : P8::NS;
+          asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(klo[i]), "+v"(khi[i]) : "n"(2 * (nis - i - 1)));
+          const i32x8 kf = i32x8{klo[i][0], klo[i][1], klo[i][2], klo[i][3],
+                                 khi[i][0], khi[i][1], khi[i][2], khi[i][3]};
+          mfma8_sa<t == 0, jb == 0>(sA[jb], kf, qf[t]);
+          if constexpr (i + AHEAD < P8::NS) rd(IC<i + AHEAD>{});
+        });
+      }
+      s_fence(sA);
+      float mx;
+      {
+        float mxj[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          mxj[j] = fmaxf(sA[j][0], sA[j][1]);
+#pragma unroll
+          for (int v = 2; v < 16; v += 2) mxj[j] = fmaxf(fmaxf(mxj[j], sA[j][v]), sA[j][v + 1]);
+        }
+        mx = max_halves(fmaxf(fmaxf(mxj[0], mxj[1]), fmaxf(mxj[2], mxj[3])));
+      }
+      // Softmax of tile kb on S(kb) (cur, AGPRs) up to the rescale factor:
+      // the same operations as the same-phase body.
+      auto head = [&](int kb, float& c_tile, float& alpha, float& f) __attribute__((always_inline)) {
+        c_tile = scale_log2 * sq * sk_bh[kb];
+        const float sv = sv_bh[kb];
+        const float m_new = fmaxf(m, mx * c_tile);
+        alpha = exp2_fast(m - m_new);
+        m = m_new;
+        f = alpha * (sv_prev * __builtin_amdgcn_rcpf(sv));
+        sv_prev = sv;
+      };
+      // Iteration j: K slot SK holds K(j+1), V slot SV holds V(j); cur = S(j),
+      // nxt receives S(j+1).
+      auto iter = [&](auto SK_, auto SV_, f32x16 (&cur)[4], f32x16 (&nxt)[4], int j)
+                      __attribute__((always_inline)) {
+        constexpr int SK = decltype(SK_)::value, SV = decltype(SV_)::value;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();  // K(j+1), V(j) landed; every wave is done with K(j), V(j-1)
+        // the next tiles' copies go out one per slot in slots 0 .. 15
+        const __amdgpu_buffer_rsrc_t rkn = tile_rsrc(kh, (uint32_t)min(j + 2, nint - 1) * kBC * row_bytes, nbytes);
+        const __amdgpu_buffer_rsrc_t rvn = tile_rsrc(vh, (uint32_t)(j + 1) * kBC * row_bytes, nbytes);
+        const bool kn = j + 2 < nint;
+        float c_tile, alpha, f;
+        head(j, c_tile, alpha, f);
+        const float neg_m = -m;
+        o8_fence<D>(oacc);  // P.V(j-1) -> the rescale
+        float rs4[4] = {0.f, 0.f, 0.f, 0.f};
+        float pe[64];
+        i32x8 pf[2];
+        i32x4 klo[P8::NS], khi[P8::NS];
+        i32x2 vr[P8::NP][4];
+        float mxj[4];
+        auto issue = [&](auto R_) __attribute__((always_inline)) {
+          constexpr int r = decltype(R_)::value;
+          if constexpr (r < 2 * P8::NS) {
+            constexpr int i = r / 2, jb = i % 4, t = i / 4;
+            if constexpr (r % 2 == 0) klo[i] = read_k16<G::koff(SK) + jb * 32 * G::RB>(kad[t][0]);
+            else khi[i] = read_k16<G::koff(SK) + jb * 32 * G::RB>(kad[t][1]);
+          } else {
+            constexpr int k = (r - 2 * P8::NS) / 4, q = (r - 2 * P8::NS) % 4, u = k / 8, e = k % 8;
+            vr[k][q] = read_tr8<G::voff(SV) + 16 * (4 * u + q) * G::RB>(vaddr[e]);
+          }
+        };
+        static_for<P8::N>([&](auto S_) __attribute__((always_inline)) {
+          constexpr int s = decltype(S_)::value;
+          if constexpr (s == 0) {
+            static_for<P8::kLook + 1>([&](auto K_) __attribute__((always_inline)) {
+              issue(IC<decltype(K_)::value>{});
+            });
+          }
+          constexpr int W = P8::issued(s - 1) - P8::need(s);
+          static_assert(W >= 0 && W <= 15, "wait count");
+          if constexpr (s < P8::NS) {
+            constexpr int jb = s % 4, t = s / 4;
+            asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(klo[s]), "+v"(khi[s]) : "n"(W));
+            const i32x8 kf = i32x8{klo[s][0], klo[s][1], klo[s][2], klo[s][3],
+                                   khi[s][0], khi[s][1], khi[s][2], khi[s][3]};
+            mfma8_sa<t == 0, jb == 0>(nxt[jb], kf, qf[t]);
+          } else {
+            constexpr int k = s - P8::NS, u = k / 8, e = k % 8;
+            asm volatile("s_waitcnt lgkmcnt(%4)"
+                         : "+v"(vr[k][0]), "+v"(vr[k][1]), "+v"(vr[k][2]), "+v"(vr[k][3])
+                         : "n"(W));
+            const i32x8 vf = i32x8{vr[k][0][0], vr[k][0][1], vr[k][1][0], vr[k][1][1],
+                                   vr[k][2][0], vr[k][2][1], vr[k][3][0], vr[k][3][1]};
+            mfma8_v<true>(oacc[e], vf, pf[u]);
+          }
+          constexpr int first = P8::issued(s - 1) + 1;
+          static_for<P8::issued(s) - P8::issued(s - 1)>([&](auto K_) __attribute__((always_inline)) {
+            issue(IC<first + decltype(K_)::value>{});
+          });
+          if constexpr (s < 2 * G::LOADS) {
+            constexpr int i = s % G::LOADS;
+            if constexpr (s < G::LOADS) {
+              if (kn) copy_to_lds16(rkn, smem + (wave * G::LOADS + i) * 1024 + G::koff(SV), voff_k[i]);
+            } else {
+              copy_to_lds16(rvn, smem + (wave * G::LOADS + i) * 1024 + G::VBASE + G::voff(SK), voff_v[i]);
+            }
+          }
+          // O^T block e = s / 2 rescaled (half of it per slot)
+          if constexpr (s < 16) {
+            constexpr int e = s / 2, h0 = 8 * (s % 2);
+#pragma unroll
+            for (int v = h0; v < h0 + 8; ++v) oacc[e][v] *= f;
+          }
+          // exponentials of S(j), in the same-phase body's order
+          static_for<64>([&](auto V_) __attribute__((always_inline)) {
+            constexpr int v = decltype(V_)::value;
+            if constexpr (P8::exp_slot(v) == s) {
+              constexpr int u = v / 32, w = (v % 32) / 4, i = v % 4;
+              constexpr int blk = 2 * u + (w >> 2), r0 = 4 * (w & 3);
+              pe[v] = exp2_fast(__builtin_fmaf(cur[blk][r0 + i], c_tile, neg_m));
+              rs4[i] += pe[v];
+              if constexpr (i == 3) {
+                pf[u][w] = (int)pack_fp8x4(pe[v - 3], pe[v - 2], pe[v - 1], pe[v]);
+                asm volatile("" : "+v"(rs4[0]), "+v"(rs4[1]), "+v"(rs4[2]), "+v"(rs4[3]), "+v"(pf[u][w]));
+              } else {
+                asm volatile("" : "+v"(pe[v]));
+              }
+            }
+          });
+          // S(j+1)'s row max, eight values per slot
+          if constexpr (s >= P8::kMax0) {
+            constexpr int b = (s - P8::kMax0) / 2, h = 8 * ((s - P8::kMax0) % 2);
+            if constexpr (s == P8::kMax0) s_fence(nxt);
+            float x = h == 0 ? fmaxf(nxt[b][0], nxt[b][1]) : fmaxf(mxj[b], fmaxf(nxt[b][h], nxt[b][h + 1]));
+#pragma unroll
+            for (int v = h + 2; v < h + 8; v += 2) x = fmaxf(fmaxf(x, nxt[b][v]), nxt[b][v + 1]);
+            mxj[b] = x;
+            asm volatile("" : "+v"(mxj[b]));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        l = l * alpha + ((rs4[0] + rs4[1]) + (rs4[2] + rs4[3]));
+        mx = max_halves(fmaxf(fmaxf(mxj[0], mxj[1]), fmaxf(mxj[2], mxj[3])));
+      };
+      int j = 0;
+      for (; j + 2 < nint - 1; j += 2) {
+        iter(IC<1>{}, IC<0>{}, sA, sB, j);
+        iter(IC<0>{}, IC<1>{}, sB, sA, j + 1);
+      }
+      iter(IC<1>{}, IC<0>{}, sA, sB, nint - 2);
+      // The last interior tile: softmax of S(nint-1) (in sB) and its P.V, V in
+      // slot (nint-1) % 2 = 1.
+      {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        float c_tile, alpha, f;
+        head(nint - 1, c_tile, alpha, f);
+        const float neg_m = -m;
+        float rs4[4] = {0.f, 0.f, 0.f, 0.f};
+        i32x8 pf[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int w = 0; w < 8; ++w) {
+            const f32x16& sa = sB[2 * u + (w >> 2)];
+            const int r0 = 4 * (w & 3);
+            float p[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              p[i] = exp2_fast(__builtin_fmaf(sa[r0 + i], c_tile, neg_m));
+              rs4[i] += p[i];
+            }
+            pf[u][w] = (int)pack_fp8x4(p[0], p[1], p[2], p[3]);
+          }
+        l = l * alpha + ((rs4[0] + rs4[1]) + (rs4[2] + rs4[3]));
+        o8_fence<D>(oacc);
+#pragma unroll
+        for (int e = 0; e < D / 32; ++e) oacc[e] *= f;
+        constexpr int NEH = 4;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          i32x8 vf[2][NEH];
+          read_vt<D, 1, NEH>(vaddr + hf * NEH, vf);
+          lds_wait_v(vf);
+          static_for<2>([&](auto U_) {
+            constexpr int u = decltype(U_)::value;
+            static_for<NEH>([&](auto E_) {
+              constexpr int e = decltype(E_)::value;
+              pv8<D, true>(oacc[hf * NEH + e], vf[u][e], pf[u]);
+            });
+          });
+        }
+      }
+      __syncthreads();  // every wave is done with the pipelined loop's tiles
+      kb2 = nint;
+    }
+  }
+  if (kb2 < nkb) LOAD_TILE(0, kb2 * kBC);
   for (; kb2 < nkb_int; kb2 += 2) {
     STEP8(0, kb2, false);
     STEP8(1, kb2 + 1, false);

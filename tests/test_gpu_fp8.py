@@ -107,6 +107,19 @@ def _rmse(a, b):
 @pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("N", [100, 256, 1000])
 def test_fp8_attention_vs_emulation_full(causal, d, N):
+    _fp8_vs_emulation(causal, d, N)
+
+
+@pytest.mark.parametrize("N", [384, 640, 1152, 1300])
+def test_fp8_d256_pipelined_vs_emulation(N):
+    """The pipelined loop of head dim 256 (non-causal) against the
+    emulation: one, three and seven iterations over the interior tiles, each
+    followed by one whole edge tile (N = 384, 640, 1152), and nine followed by
+    a ragged tail (N = 1300)."""
+    _fp8_vs_emulation(False, 256, N)
+
+
+def _fp8_vs_emulation(causal, d, N):
     w = workloads.Workload(f"fp8_n{N}_d{d}", 2, 3, N, d, causal, seed=50 + N, dist="outlier_sd10")
     say(w.name + ("_causal" if causal else ""))
     q, k, v = _bf16_host(w)
