@@ -411,9 +411,9 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
     // count, at least two; the edge tiles follow in the loops below).  K(j)
     // sits in K slot j % R and V(j) in V slot j % R, K loaded one tile ahead:
     // iteration j reads K(j+1) and V(j).  R = 2: it starts the copies of
-    // K(j+2) and V(j+1) after its barrier, which certifies that K(j+1) and
-    // V(j) have landed and that every wave is done with the slots of K(j) and
-    // V(j-1).  R = 4: it ends by starting the copies of K(j+3) and V(j+2) (of
+    // K(j+2) and V(j+1) (one per slot in its first slots) after its barrier,
+    // which certifies that K(j+1) and V(j) have landed and that every wave is
+    // done with the slots of K(j) and V(j-1).  R = 4: it ends by starting the copies of K(j+3) and V(j+2) (of
     // tile nint - 1 again where those are past the interior, so that every
     // iteration has the same copies in flight), and its barrier, fence-free,
     // follows a wait that leaves the last iteration's copies in flight.
@@ -491,9 +491,15 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
         } else {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           __syncthreads();
-          if (j + 2 < nint) load_k(SV, (j + 2) * kBC);
-          if (j + 1 < nint) load_v(SK, (j + 1) * kBC);
         }
+        // R = 2: the next tiles' copies go out one per slot in the first slots,
+        // under the MFMAs (issued together after the barrier they stalled the
+        // wave: at d = 256 sixteen 1 KB copies per wave; +7.6% at d = 256,
+        // +6% on the 4-wave workgroups at d = 128)
+        const __amdgpu_buffer_rsrc_t rkn =
+            tile_rsrc(kh, (uint32_t)min(j + 2, nint - 1) * kBC * row_bytes, nbytes);
+        const __amdgpu_buffer_rsrc_t rvn = tile_rsrc(vh, (uint32_t)(j + 1) * kBC * row_bytes, nbytes);
+        const bool kn = j + 2 < nint;
         raise_offset(mx);
         const float neg_m = -m;
         float rsum = 0.f;
@@ -542,6 +548,14 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
           static_for<P::issued(s) - P::issued(s - 1)>([&](auto K_) __attribute__((always_inline)) {
             issue(IC<first + decltype(K_)::value>{});
           });
+          if constexpr (R == 2 && s < 2 * LOADS) {
+            constexpr int i = s % LOADS;
+            if constexpr (s < LOADS) {
+              if (kn) copy_to_lds16(rkn, smem + (wave * LOADS + i) * 1024 + RG::k(SV), voff_k[i]);
+            } else {
+              copy_to_lds16(rvn, smem + (wave * LOADS + i) * 1024 + G::VBASE + RG::v(SK), voff_v[i]);
+            }
+          }
           static_for<32>([&](auto E_) __attribute__((always_inline)) {
             constexpr int v = decltype(E_)::value;
             if constexpr (P::exp_slot(v) == s) {
