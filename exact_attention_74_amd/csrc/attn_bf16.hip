@@ -14,8 +14,8 @@
 // per SIMD, with O in the AGPR file.  The interior key tiles run software-
 // pipelined (the next tile's S MFMAs issued between the current tile's
 // exponentials, report section 3.2): non-causal at every head dim, causal on
-// the 8-wave workgroups (d = 64 and 128); every other case runs the
-// same-phase loop (both waves of a SIMD do MFMAs, then both do softmax).
+// the 8-wave workgroups and at d = 256; every other case runs the same-phase
+// loop (both waves of a SIMD do MFMAs, then both do softmax).
 //
 // Transposed formulation.  Each wave computes S^T = K Q^T (keys as MFMA rows,
 // its 32 queries as MFMA columns), so the accumulator keeps every query on one
@@ -219,9 +219,9 @@ __device__ __forceinline__ void tile_compute(const char* smem, const uint32_t (&
 }
 
 // Software-pipelined interior tiles (non-causal at every head dim and on
-// both workgroup sizes; causal on the 8-wave workgroups, up to a block's
-// diagonal; the same-phase loop below serves the edge tiles and every other
-// case).  The FlashAttention-3 report (section 3.2) issues the next block's
+// both workgroup sizes; causal on the 8-wave workgroups and at d = 256, up to
+// a block's diagonal; the same-phase loop below serves the edge tiles and
+// every other case).  The FlashAttention-3 report (section 3.2) issues the next block's
 // S = Q K^T before the current block's softmax so that the matrix cores work
 // while the exponentials run.  Here iteration j of a wave issues its MFMAs one
 // per slot: the NS of S(j+1) = K(j+1) Q^T, then the NP of
@@ -841,10 +841,10 @@ template <int D, bool CAUSAL, bool PIPE = false>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                   int Hkv, int N, float scale, hipStream_t stream) {
   // d = 256: one wave per SIMD (Q fragments and O take 192 registers), so
-  // always four waves; the pipelined loop non-causal (+11.6% at B2 H16
-  // N8192), the same-phase loop causal.
+  // always four waves, with the pipelined loop (+11.6% at B2 H16 N8192,
+  // causal +14%).
   if constexpr (D > 128) {
-    return launch_nw<D, CAUSAL, 4, PIPE && !CAUSAL>(q, k, v, o, lse, B, H, Hkv, N, scale, stream);
+    return launch_nw<D, CAUSAL, 4, PIPE>(q, k, v, o, lse, B, H, Hkv, N, scale, stream);
   } else {
     const int small_n = (CAUSAL ? 4096 : 1024) * (128 / D);
     // the pipelined loop on the 4-wave workgroups: non-causal only (+2-3% at
@@ -862,17 +862,18 @@ hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, voi
                                 int B, int H, int Hkv, int N, int d, bool causal,
                                 float softmax_scale, hipStream_t stream, bool same_phase) {
   // The pipelined loop (the same results as the same-phase loop, measured
-  // 1-4% faster at d = 64 and 128, 12% at d = 256): non-causal at every head
-  // dim and workgroup size, causal on the 8-wave workgroups (d = 64 and 128);
-  // same_phase selects the same-phase loop there too, for comparison.
+  // 1-4% faster at d = 64 and 128, 12-14% at d = 256): non-causal at every
+  // head dim and workgroup size, causal on the 8-wave workgroups and at
+  // d = 256; same_phase selects the same-phase loop there too, for comparison.
   if (!same_phase && d == 128)
     return causal ? launch<128, true, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream)
                   : launch<128, false, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream);
   if (!same_phase && d == 64)
     return causal ? launch<64, true, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream)
                   : launch<64, false, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream);
-  if (!same_phase && d == 256 && !causal)
-    return launch<256, false, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream);
+  if (!same_phase && d == 256)
+    return causal ? launch<256, true, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream)
+                  : launch<256, false, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream);
   if (d == 256)
     return causal ? launch<256, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream)
                   : launch<256, false>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream);

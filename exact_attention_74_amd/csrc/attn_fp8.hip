@@ -164,7 +164,8 @@ __device__ __forceinline__ void o8_fence(f32x16 (&o)[D / 32]) {
 }
 
 
-// Software-pipelined interior tiles at head dim 256 (non-causal): one wave
+// Software-pipelined interior tiles at head dim 256 (causal: the tiles
+// before a block's diagonal): one wave
 // per SIMD, so no second wave's MFMAs cover the softmax; instead iteration j
 // of a wave issues its MFMAs one per slot, the 16 of S(j+1) = K(j+1) Q^T and
 // then the 16 of O^T += V(j)^T P(j)^T, with tile j's softmax (the exponentials,
@@ -437,7 +438,7 @@ _Pragma("unroll")                                                               
   const int nkb_int = min(nkb, min(CAUSAL ? qblk * (kBR / kBC) : nkb, N / kBC)) & ~1;
 
   int kb2 = 0;
-  if constexpr (D > 128 && !CAUSAL) {
+  if constexpr (D > 128) {
     if (nkb_int >= 2) {
       namespace P8 = fpipe8;
       const int nint = nkb_int;

@@ -293,19 +293,34 @@ def test_pipelined_full_parity(N, d):
     _check(o, lse, o_ref, lse_ref, w.name, absv)
 
 
+@pytest.mark.parametrize("N", [300, 640, 1000])
+def test_pipelined_causal_d256_full_parity(N):
+    """Causal head dim 256: the pipelined loop over each block's tiles
+    before its diagonal (blocks 1 and up), the same-phase loop over the
+    diagonal and ragged tiles; every element against the oracle, and
+    bit-identical to the same-phase schedule."""
+    w = workloads.Workload(f"pipe_c_n{N}_d256", 1, 3, N, 256, True, seed=43 + N)
+    say(w.name)
+    host, dev = bf16_inputs(w)
+    o, lse = _default_vs_same_phase(dev, True, w.softmax_scale)
+    o_ref, lse_ref = oracle.naive_attention(*host, w.softmax_scale, True)
+    absv, _ = oracle.naive_attention(host[0], host[1], np.abs(host[2]), w.softmax_scale, True)
+    _check(o, lse, o_ref, lse_ref, w.name, absv)
+
+
 @pytest.mark.parametrize("B,H,N,d,causal", [(2, 16, 8192, 128, False), (2, 4, 8192, 128, True),
                                             (1, 3, 5000, 128, True), (1, 2, 8300, 64, True),
                                             (1, 4, 1024, 128, False),
                                             (1, 3, 3000, 64, False), (1, 3, 3000, 128, True),
                                             (1, 2, 700, 256, True), (2, 8, 8192, 256, False),
-                                            (2, 2, 1, 128, False)])
+                                            (2, 8, 8192, 256, True), (2, 2, 1, 128, False)])
 def test_schedules_sampled_rows(B, H, N, d, causal):
-    """The bench shapes B2 H16 N8192 (d = 128) and B2 H8 N8192 (d = 256),
-    d = 64 N = 3000 and causal N = 5000, 8192 (d = 128) and 8300 (d = 64)
-    through the pipelined loop (sampled rows against the oracle; causal blocks
-    run it up to their diagonal), and the shapes that run the same-phase loop
-    under both entry points (short N, causal d = 128 N <= 4096, causal
-    d = 256, one token): bit-identical."""
+    """The bench shapes B2 H16 N8192 (d = 128) and B2 H8 N8192 (d = 256, both
+    masks), d = 64 N = 3000, causal N = 5000, 8192 (d = 128), 8300 (d = 64)
+    and 700 (d = 256) through the pipelined loop (sampled rows against the
+    oracle; causal blocks run it up to their diagonal), and the shapes that
+    run the same-phase loop under both entry points (short N, causal d = 128
+    N <= 4096, one token): bit-identical."""
     w = workloads.Workload(f"sched_b{B}h{H}n{N}d{d}", B, H, N, d, causal, seed=7 + N)
     say(w.name + ("_causal" if causal else ""))
     host, dev = bf16_inputs(w)

@@ -110,13 +110,15 @@ def test_fp8_attention_vs_emulation_full(causal, d, N):
     _fp8_vs_emulation(causal, d, N)
 
 
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [384, 640, 1152, 1300])
-def test_fp8_d256_pipelined_vs_emulation(N):
-    """The pipelined loop of head dim 256 (non-causal) against the
-    emulation: one, three and seven iterations over the interior tiles, each
+def test_fp8_d256_pipelined_vs_emulation(causal, N):
+    """The pipelined loop of head dim 256 against the emulation.
+    Non-causal: one, three and seven iterations over the interior tiles, each
     followed by one whole edge tile (N = 384, 640, 1152), and nine followed by
-    a ragged tail (N = 1300)."""
-    _fp8_vs_emulation(False, 256, N)
+    a ragged tail (N = 1300).  Causal: the blocks' tiles before their
+    diagonal (query blocks 2 and up), then the diagonal and ragged tiles."""
+    _fp8_vs_emulation(causal, 256, N)
 
 
 def _fp8_vs_emulation(causal, d, N):
