@@ -146,12 +146,26 @@ def cpu_baseline(w, target_s: float):
     }
 
 
+WARM_SECONDS = 0.025
+
+
 def time_reps(fn, reps: int, stream) -> float:
     """Median seconds of ``reps`` launches of ``fn``, each bracketed by HIP
-    events on ``stream``, after three untimed ones."""
+    events on ``stream``, after untimed launches that take about
+    WARM_SECONDS (at least three).  The warm-up puts the GPU in its sustained
+    state for this shape: with three untimed launches only, the medians moved
+    with the number of timed ones (10 vs 40 launches: 1133 vs 1225 TFLOP/s at
+    B2 H16 N8192, 862 vs 746 at B32 N512, whose short bursts still ran at the
+    boost clock)."""
     import numpy as np
     import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
     for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    per = (time.perf_counter() - t0) / 3
+    for _ in range(max(0, math.ceil(WARM_SECONDS / max(per, 1e-6)) - 3)):
         fn()
     ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
           for _ in range(reps)]
