@@ -52,9 +52,11 @@ def _gate(o, lse, o_ref, lse_ref, tag):
 @pytest.mark.parametrize("N,d,H,Hkv,causal", [
     (200, 128, 6, 3, False), (200, 128, 6, 3, True),
     (1000, 64, 8, 1, False), (1000, 128, 4, 2, True),
-    (1500, 128, 8, 2, False), (1500, 64, 4, 1, True), (500, 256, 4, 2, True)])
+    (1500, 128, 8, 2, False), (1500, 64, 4, 1, True), (500, 256, 4, 2, True),
+    (700, 256, 4, 1, False)])
 def test_bf16_gqa_full_parity(N, d, H, Hkv, causal):
-    """Full oracle parity; N = 1500 takes the 8-wave workgroups, ragged tails."""
+    """Full oracle parity; N = 1500 takes the 8-wave workgroups, d = 256 the
+    pipelined loop with O in the AGPRs (both masks), ragged tails."""
     tag = f"gqa_bf16_n{N}_d{d}_h{H}kv{Hkv}" + ("_causal" if causal else "")
     say(tag)
     q, k, v = _host(2, N, H, Hkv, d, seed=90 + N + H)
@@ -105,7 +107,8 @@ def _rmse(a, b):
 
 
 @pytest.mark.parametrize("N,d,H,Hkv,causal", [(300, 128, 6, 2, False), (1000, 64, 4, 1, True),
-                                               (1000, 128, 8, 2, True), (600, 256, 4, 2, True)])
+                                               (1000, 128, 8, 2, True), (600, 256, 4, 2, True),
+                                               (700, 256, 4, 2, False)])
 def test_fp8_gqa_vs_emulation(N, d, H, Hkv, causal):
     tag = f"gqa_fp8_n{N}_d{d}_h{H}kv{Hkv}" + ("_causal" if causal else "")
     say(tag)
