@@ -8,7 +8,7 @@
 // workgroup's start-up and epilogue overlap the other's key tiles).  The
 // key/value sequence is streamed in blocks of 64 keys with the online-softmax
 // recurrence of the FlashAttention-3 report, section 3 (running max m,
-// running sum l, one final normalisation).  Causal work at d <= 128 runs on
+// running sum l, one final normalisation).  Causal work runs on
 // persistent workgroup slots over pairs of query blocks of equal total cost
 // (see the kernel below).  Head dim 256 runs 4-wave workgroups, one wave
 // per SIMD, with O in the AGPR file.  The interior key tiles run software-
@@ -291,10 +291,11 @@ constexpr int ring() { return NW == 8 ? 4 : 2; }
 
 // One workgroup's work item: query block qblk (32 * NW rows) of head bh,
 // against every visible key.
-// Causal work runs persistent (d <= 128; at d = 256 the loop around the
-// body would push the one-wave-per-SIMD kernel into spilling).
+// Causal work runs persistent at every head dim (at d = 256 since O moved to
+// the AGPR file: the loop around the body no longer spills; +4% at B2 H16
+// N8192, +16% at B8 H16 N2048).
 template <int D, bool CAUSAL>
-constexpr bool persistent() { return CAUSAL && D <= 128; }
+constexpr bool persistent() { return CAUSAL; }
 
 template <int D, bool CAUSAL, int NW, bool PIPE>
 __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restrict__ Q,
