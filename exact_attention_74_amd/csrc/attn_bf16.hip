@@ -13,9 +13,9 @@
 // (see the kernel below).  Head dim 256 runs 4-wave workgroups, one wave
 // per SIMD, with O in the AGPR file.  The interior key tiles run software-
 // pipelined (the next tile's S MFMAs issued between the current tile's
-// exponentials, report section 3.2): non-causal at every head dim, causal on
-// the 8-wave workgroups and at d = 256; every other case runs the same-phase
-// loop (both waves of a SIMD do MFMAs, then both do softmax).
+// exponentials, report section 3.2): non-causal everywhere, causal from
+// N = 1024; every other case runs the same-phase loop (both waves of a SIMD
+// do MFMAs, then both do softmax).
 //
 // Transposed formulation.  Each wave computes S^T = K Q^T (keys as MFMA rows,
 // its 32 queries as MFMA columns), so the accumulator keeps every query on one
@@ -219,9 +219,8 @@ __device__ __forceinline__ void tile_compute(const char* smem, const uint32_t (&
 }
 
 // Software-pipelined interior tiles (non-causal at every head dim and on
-// both workgroup sizes; causal on the 8-wave workgroups and at d = 256, up to
-// a block's diagonal; the same-phase loop below serves the edge tiles and
-// every other case).  The FlashAttention-3 report (section 3.2) issues the next block's
+// both workgroup sizes; causal from N = 1024, up to a block's diagonal; the
+// same-phase loop below serves the edge tiles and every other case).  The FlashAttention-3 report (section 3.2) issues the next block's
 // S = Q K^T before the current block's softmax so that the matrix cores work
 // while the exponentials run.  Here iteration j of a wave issues its MFMAs one
 // per slot: the NS of S(j+1) = K(j+1) Q^T, then the NP of
@@ -848,11 +847,14 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
     return launch_nw<D, CAUSAL, 4, PIPE>(q, k, v, o, lse, B, H, Hkv, N, scale, stream);
   } else {
     const int small_n = (CAUSAL ? 4096 : 1024) * (128 / D);
-    // the pipelined loop on the 4-wave workgroups: non-causal only (+2-3% at
-    // N = 512-2048; causal, whose short blocks have few interior tiles, lost
-    // 3-5% at N = 512-1024)
-    if (N <= small_n)
-      return launch_nw<D, CAUSAL, 4, PIPE && !CAUSAL>(q, k, v, o, lse, B, H, Hkv, N, scale, stream);
+    // the pipelined loop on the 4-wave workgroups: non-causal at every N;
+    // causal from N = 1024 (+2-9% at N = 1024-8192; at N = 512 the blocks
+    // have too few interior tiles: -5.5%)
+    if (N <= small_n) {
+      if (CAUSAL && N < 1024)
+        return launch_nw<D, CAUSAL, 4, false>(q, k, v, o, lse, B, H, Hkv, N, scale, stream);
+      return launch_nw<D, CAUSAL, 4, PIPE>(q, k, v, o, lse, B, H, Hkv, N, scale, stream);
+    }
     return launch_nw<D, CAUSAL, 8, PIPE>(q, k, v, o, lse, B, H, Hkv, N, scale, stream);
   }
 }
@@ -863,9 +865,9 @@ hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, voi
                                 int B, int H, int Hkv, int N, int d, bool causal,
                                 float softmax_scale, hipStream_t stream, bool same_phase) {
   // The pipelined loop (the same results as the same-phase loop, measured
-  // 1-4% faster at d = 64 and 128, 12-14% at d = 256): non-causal at every
-  // head dim and workgroup size, causal on the 8-wave workgroups and at
-  // d = 256; same_phase selects the same-phase loop there too, for comparison.
+  // 1-9% faster at d = 64 and 128, 12-14% at d = 256): non-causal at every
+  // head dim and workgroup size, causal from N = 1024; same_phase selects the
+  // same-phase loop there too, for comparison.
   if (!same_phase && d == 128)
     return causal ? launch<128, true, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream)
                   : launch<128, false, true>(q, k, v, o, lse, B, H, Hkv, N, softmax_scale, stream);

@@ -88,7 +88,7 @@ int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* l
  * attn_fwd_bf16 with the same-phase schedule everywhere: both waves of a SIMD
  * issue a key tile's matrix products, then both run its softmax, one barrier
  * per tile.  attn_fwd_bf16 (and attn_fwd_bf16_gqa) use this schedule causal
- * with N <= 4096 (d = 128) or N <= 8192 (d = 64); in
+ * with N < 1024; in
  * every other case they run the intra-wave pipelined schedule of the
  * FlashAttention-3 report, section 3.2, over a block's interior key tiles:
  * each wave issues the matrix products of S(j+1) = Q K(j+1)^T and of

@@ -314,15 +314,16 @@ def test_pipelined_causal_d256_full_parity(N):
                                             (1, 3, 3000, 64, False), (1, 3, 3000, 128, True),
                                             (1, 2, 700, 256, True), (2, 8, 8192, 256, False),
                                             (2, 8, 8192, 256, True), (2, 8, 4000, 256, True),
+                                            (2, 4, 700, 128, True), (2, 4, 1500, 64, True),
                                             (2, 2, 1, 128, False)])
 def test_schedules_sampled_rows(B, H, N, d, causal):
     """The bench shapes B2 H16 N8192 (d = 128) and B2 H8 N8192 (d = 256, both
     masks), d = 64 N = 3000, causal N = 5000, 8192 (d = 128), 8300 (d = 64)
-    and 700, 4000 (d = 256; 4000: persistent slots, ragged) through the
+    and 700, 4000 (d = 256; 4000: persistent slots, ragged), and the 4-wave
+    causal workgroups at N = 3000 (d = 128) and 1500 (d = 64) through the
     pipelined loop (sampled rows against the oracle; causal blocks run it up
-    to their diagonal), and the shapes that
-    run the same-phase loop under both entry points (short N, causal d = 128
-    N <= 4096, one token): bit-identical."""
+    to their diagonal), and the shapes that run the same-phase loop under both
+    entry points (causal N < 1024, one token): bit-identical."""
     w = workloads.Workload(f"sched_b{B}h{H}n{N}d{d}", B, H, N, d, causal, seed=7 + N)
     say(w.name + ("_causal" if causal else ""))
     host, dev = bf16_inputs(w)
