@@ -11,7 +11,7 @@ Entry points (same names as the C ABI):
   blockquant_hadamard(x, signs=None, block_rows=128) -> (x8, scale)
   attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal=False, softmax_scale=None) -> (o, lse)
   attn_fwd_bf16_same_phase(q, k, v, causal=False, softmax_scale=None) -> (o, lse): the same
-    results from the same-phase schedule (attn_fwd_bf16 pipelines d = 64 and 128)
+    results from the same-phase schedule (attn_fwd_bf16 pipelines the interior key tiles)
   attn_fwd_bf16_gqa / attn_fwd_fp8_gqa: the same with K/V (and their scales) on
     H_kv heads, H a multiple of H_kv (grouped-query / multi-query attention).
   attn_bwd_bf16(q, k, v, o, lse, do, causal=False, softmax_scale=None) -> (dq, dk, dv)
@@ -168,7 +168,8 @@ def attn_fwd_bf16(q, k, v, causal: bool = False, softmax_scale: float | None = N
 def attn_fwd_bf16_same_phase(q, k, v, causal: bool = False, softmax_scale: float | None = None,
                              out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
     """attn_fwd_bf16 with the same-phase schedule everywhere (attn_fwd_bf16
-    pipelines d = 64 and 128 on long sequences); results bit-identical to it."""
+    pipelines the interior key tiles: non-causal everywhere, causal from N = 1024);
+    results bit-identical to it."""
     return _bf16("attn_fwd_bf16_same_phase", q, k, v, causal, softmax_scale, out, lse)
 
 
