@@ -444,8 +444,9 @@ __device__ __forceinline__ void attend_block(char* smem, const __bf16* __restric
 #pragma unroll
         for (int e = 0; e < D / 32; ++e) vaddr[e] += RG::VB;
       } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+        // K(0) landed (V(0) and K(1) may still be in flight: S(0) overlaps them)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LOADS) : "memory");
+        __builtin_amdgcn_s_barrier();
       }
       // S(0) ahead of the loop, as in the same-phase tile body.
       f32x16 sA[2], sB[2];

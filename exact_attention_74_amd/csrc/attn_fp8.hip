@@ -464,8 +464,9 @@ _Pragma("unroll")                                                               
       load_k(0, 0);
       load_v(0, 0);
       load_k(1, kBC);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
+      // K(0) landed (V(0) and K(1) may still be in flight: S(0) overlaps them)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * G::LOADS) : "memory");
+      __builtin_amdgcn_s_barrier();
       f32x16 sA[4], sB[4];
       // S(0) = K(0) Q^T (K slot 0), then its row max
       {
