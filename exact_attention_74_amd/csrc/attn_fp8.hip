@@ -502,9 +502,16 @@ _Pragma("unroll")                                                               
       }
       // Softmax of tile kb on S(kb) (cur, AGPRs) up to the rescale factor:
       // the same operations as the same-phase body.
+      // Tile kb's block scales were loaded at the end of the previous
+      // iteration (prefetch below); their scalar-load wait comes here, right
+      // after the barrier, with no LDS read in flight.
+      float skp = sk_bh[0], svp = sv_bh[0];
       auto head = [&](int kb, float& c_tile, float& alpha, float& f) __attribute__((always_inline)) {
-        c_tile = scale_log2 * sq * sk_bh[kb];
-        const float sv = sv_bh[kb];
+        (void)kb;
+        float skc = skp, svc = svp;
+        asm volatile("" : "+s"(skc), "+s"(svc));
+        c_tile = scale_log2 * sq * skc;
+        const float sv = svc;
         const float m_new = fmaxf(m, mx * c_tile);
         alpha = exp2_fast(m - m_new);
         m = m_new;
@@ -615,6 +622,8 @@ _Pragma("unroll")                                                               
         });
         l = l * alpha + ((rs4[0] + rs4[1]) + (rs4[2] + rs4[3]));
         mx = max_halves(fmaxf(fmaxf(mxj[0], mxj[1]), fmaxf(mxj[2], mxj[3])));
+        skp = sk_bh[j + 1];  // the next tile's scales (tile j + 1 <= nint - 1 exists)
+        svp = sv_bh[j + 1];
       };
       int j = 0;
       for (; j + 2 < nint - 1; j += 2) {
