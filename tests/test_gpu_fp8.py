@@ -248,14 +248,15 @@ def test_fp8_d256_full_size_sampled_rows(causal):
 
 
 @pytest.mark.parametrize("B,H,N,d", [(2, 16, 5000, 128), (3, 5, 3000, 64), (2, 8, 8192, 128),
-                                     (4, 16, 4096, 128)])
+                                     (4, 16, 4096, 128), (1, 8, 32768, 128)])
 def test_fp8_causal_schedules_sampled_rows(B, H, N, d):
     """Causal FP8 work in both schedules.  One workgroup per query block:
     B2 H16 N5000 (its 320 equal-cost block pairs would leave the second round
     of 256 slots a quarter full) and B3 H5 N3000 d64 (180 blocks, fewer than
-    the CUs).  Persistent slots over block pairs: B2 H8 N8192 (one round) and
-    B4 H16 N4096 (two).  Sampled rows against the emulation, and a second run
-    bit for bit."""
+    the CUs).  Persistent slots over block pairs: B2 H8 N8192 (one round),
+    B4 H16 N4096 (two) and the long single request B1 H8 N32768 (512 pairs of
+    up to 256 key tiles each).  Sampled rows against the emulation, and a
+    second run bit for bit."""
     w = workloads.Workload(f"fp8_causal_sched_b{B}h{H}n{N}d{d}", B, H, N, d, True, seed=70 + N,
                            dist="outlier_sd10")
     say(w.name)
