@@ -68,3 +68,24 @@ def test_no_alloc_matches_workspace_entry_point_twice():
             e = to_np(g) - r
             assert np.sqrt(np.mean(e ** 2)) <= 1e-2 * np.sqrt(np.mean(r ** 2)), name
 
+
+
+def test_no_alloc_at_the_scratch_limit():
+    """B H N = 2^21 rows: the per-row workspace (8 bytes a row) fills the
+    scratch array exactly.  Bit for bit against the workspace entry point;
+    inputs drawn on the device (no oracle is involved in this comparison)."""
+    B, H, N, d = 8, 16, 16384, 128
+    assert 8 * B * H * N == ea.NOALLOC_SCRATCH_BYTES
+    say(f"noalloc at the scratch limit b{B}h{H}n{N}d{d}")
+    g = torch.Generator(device=DEV).manual_seed(11)
+    q, k, v, do = (torch.randn((B, N, H, d), generator=g, device=DEV).to(torch.bfloat16)
+                   for _ in range(4))
+    scale = d ** -0.5
+    o, lse = ea.attn_fwd_bf16(q, k, v, causal=True, softmax_scale=scale)
+    t = (q, k, v, o, do, lse)
+    want = _with_workspace(t, B, H, H, N, d, True, scale)
+    got = _no_alloc(t, B, H, H, N, d, True, scale)
+    torch.cuda.synchronize()
+    for name, x, y in zip(("dq", "dk", "dv"), got, want):
+        assert torch.isfinite(x.float()).all(), name
+        assert torch.equal(x, y), name
